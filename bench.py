@@ -1,0 +1,201 @@
+"""Benchmark of the fused exact attention (forward + backward) on one MI355X.
+
+One step = attn_fwd followed by the backward stages (preprocess, dq, dkdv) on
+one batch of the headline workload, B=2, H=32, N=8192, d=128, bf16, causal,
+with inputs already resident in device memory.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
+                    [--no-cpu-baseline]
+
+Reported:
+  value         whole-step attention TFLOP/s, (F_fwd + F_bwd) / t_step, with the
+                algorithmic FLOP counts 4*B*H*N^2*d (halved when causal) and
+                2.5x that for the backward
+  fwd_tflops    forward alone, from HIP events around attn_fwd
+  roofline      the kernel with the largest share of the step, against the
+                bf16 dense MFMA peak; its average launch time comes from HIP
+                events recorded around it inside the timed steps
+  cpu_baseline  the fp64 CPU oracle, timed on a bounded sample of heads
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bf16_n8192_d128_causal")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_flops(w: W.Workload):
+    """Algorithmic FLOPs each launch performs, by kernel.
+
+    A forward contraction over the allowed (query, key) pairs costs
+    2*B*H*N^2*d (halved when causal); the forward has two, the backward five
+    (the recomputed Q K^T, dO V^T, P^T dO, dS^T Q and dS K).  dkdv executes four
+    of the five; dq executes dS K (its recomputed Q K^T, dO V^T and the P K
+    correction are not counted); preprocess is memory traffic only.
+    """
+    one = w.fwd_flops() / 2
+    return {"fwd": 2 * one, "dkdv": 4 * one, "dq": 1 * one, "preprocess": 0.0}
+
+
+def cpu_baseline(w: W.Workload, budget_s: float):
+    """Time the fp64 oracle (forward + backward) head by head for about budget_s."""
+    import numpy as np
+    from oracle import attention as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    inp = W.draw(1, 1, w.N, w.d, w.dtype, seed=w.seed + 77)
+    q, k, v, do = (inp[x][0, 0].float().numpy().astype(np.float64) for x in ("q", "k", "v", "do"))
+    heads = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.forward_head(q, k, v, w.scale, w.causal)
+        orc.backward_head(q, k, v, do, w.scale, w.causal)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    per_head = (w.fwd_flops() + w.bwd_flops()) / (w.B * w.H)
+    return {
+        "value": per_head * heads / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{heads} head(s) of the workload (N={w.N}, d={w.d}, causal={w.causal}), forward + backward "
+                  f"in fp64 with S and P materialised, {dt:.1f} s; rate counts the same algorithmic FLOPs as value",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(every (batch, head) pair is independent, so N GPUs would each run B*H/N heads).", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    import exact_io_aware_23_amd as A
+
+    A.load_library()
+    w = W.BY_NAME[args.workload]
+    dev = torch.device("cuda", 0)
+    inp = W.draw_workload(w)
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    delta_exact = torch.empty_like(delta)
+    stream = torch.cuda.current_stream(dev)
+    names = ["fwd", "preprocess", "dq", "dkdv"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        A.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        A.bwd_preprocess(o, do, delta)
+        if ev is not None:
+            ev[2].record(stream)
+        A.bwd_dq(q, k, v, lse, do, delta, scale=w.scale, causal=w.causal, dq=dq, delta_out=delta_exact)
+        if ev is not None:
+            ev[3].record(stream)
+        A.bwd_dkdv(q, k, v, lse, do, delta_exact, scale=w.scale, causal=w.causal, dk=dk, dv=dv)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_kernel = {n: 0.0 for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per_kernel[n] += ev[j].elapsed_time(ev[j + 1])
+    per_kernel = {n: t / args.steps for n, t in per_kernel.items()}  # ms per launch
+    gpu_ms = events[0][0].elapsed_time(events[-1][4]) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    F_fwd, F_bwd = w.fwd_flops(), w.bwd_flops()
+    value = (F_fwd + F_bwd) / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = F_fwd / (per_kernel["fwd"] * 1e-3) / 1e12
+    bwd_ms = per_kernel["preprocess"] + per_kernel["dq"] + per_kernel["dkdv"]
+    bwd_tflops = F_bwd / (bwd_ms * 1e-3) / 1e12
+
+    kf = kernel_flops(w)
+    dominant = max(names, key=lambda n: per_kernel[n])
+    achieved = kf[dominant] / (per_kernel[dominant] * 1e-3) / 1e12
+    traffic = None
+    roof = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+            "avg_launch_ms": round(per_kernel[dominant], 4)}
+
+    out = {
+        "metric": "attention TFLOP/s fwd and fwd+bwd (bf16, N=8192 d=128 causal) + % MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "pass": "fwd+bwd"},
+        "fwd_tflops": round(fwd_tflops, 2),
+        "fwd_frac_mfma_peak": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "bwd_tflops": round(bwd_tflops, 2),
+        "fwdbwd_frac_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,189 @@
+"""ctypes binding of libattn.so; names follow the C ABI in include/attn.h."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_F32, ATTN_BF16 = 0, 1
+
+_lib = None
+_lock = threading.Lock()
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+
+_SIGNATURES = {
+    "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_workspace_bytes": (_S, [_I, _I, _I, _I]),
+    "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_preprocess": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_status_string": (ctypes.c_char_p, [_I]),
+    "attn_abi_version": (_I, []),
+}
+
+
+class AttnError(RuntimeError):
+    """A non-OK status from the C ABI."""
+
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+
+
+def load_library(path: str | None = None):
+    """Load libattn.so (built in-tree by exact_io_aware_23_amd.build) once."""
+    global _lib
+    with _lock:
+        if _lib is not None and path is None:
+            return _lib
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing: build it with `python -m exact_io_aware_23_amd.build`")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().attn_status_string(status).decode()
+
+
+def abi_version() -> int:
+    return load_library().attn_abi_version()
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return load_library().attn_bwd_workspace_bytes(B, H, N, d)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(name: str, t: torch.Tensor, shape, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _call(name: str, *args):
+    st = getattr(load_library(), name)(*args)
+    if st != ATTN_OK:
+        raise AttnError(name, st)
+
+
+def _default_scale(d: int, scale):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None, causal: bool = False,
+        out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """attn_fwd on [B, H, N, d] tensors; returns (O, L) with L fp32 [B, H, N]."""
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check("out", out, (B, H, N, d), q.dtype)
+    _check("lse", lse, (B, H, N), torch.float32)
+    _call("attn_fwd", q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+          _dtype_code(q), _default_scale(d, scale), int(bool(causal)), _stream(q.device))
+    return out, lse
+
+
+def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, workspace=None,
+        dq=None, dk=None, dv=None):
+    """attn_bwd; returns (dQ, dK, dV)."""
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    _check("lse", lse, (B, H, N), torch.float32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    ws_bytes = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _call("attn_bwd", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, N, d,
+          _dtype_code(q), _default_scale(d, scale), int(bool(causal)), _stream(q.device))
+    return dq, dk, dv
+
+
+def bwd_preprocess(o, do, delta=None):
+    """attn_bwd_preprocess; returns delta fp32 [B, H, N]."""
+    B, H, N, d = o.shape
+    _check("do", do, (B, H, N, d), o.dtype)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=o.device) if delta is None else delta
+    _check("delta", delta, (B, H, N), torch.float32)
+    _call("attn_bwd_preprocess", o.data_ptr(), do.data_ptr(), delta.data_ptr(), B, H, N, d, _dtype_code(o),
+          _stream(o.device))
+    return delta
+
+
+def bwd_dkdv(q, k, v, lse, do, delta, scale: float | None = None, causal: bool = False, dk=None, dv=None):
+    """attn_bwd_dkdv; returns (dK, dV)."""
+    B, H, N, d = q.shape
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("k", k), ("v", v), ("do", do), ("dk", dk), ("dv", dv)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    _check("lse", lse, (B, H, N), torch.float32)
+    _check("delta", delta, (B, H, N), torch.float32)
+    _call("attn_bwd_dkdv", q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
+          delta.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, _dtype_code(q), _default_scale(d, scale),
+          int(bool(causal)), _stream(q.device))
+    return dk, dv
+
+
+def bwd_dq(q, k, v, lse, do, delta, scale: float | None = None, causal: bool = False, dq=None,
+           delta_out=None):
+    """attn_bwd_dq; returns (dQ, exact delta)."""
+    B, H, N, d = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    delta_out = torch.empty_like(delta) if delta_out is None else delta_out
+    for name, t in (("k", k), ("v", v), ("do", do), ("dq", dq)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    _check("lse", lse, (B, H, N), torch.float32)
+    _check("delta", delta, (B, H, N), torch.float32)
+    _check("delta_out", delta_out, (B, H, N), torch.float32)
+    _call("attn_bwd_dq", q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
+          delta.data_ptr(), dq.data_ptr(), delta_out.data_ptr(), B, H, N, d, _dtype_code(q),
+          _default_scale(d, scale), int(bool(causal)), _stream(q.device))
+    return dq, delta_out

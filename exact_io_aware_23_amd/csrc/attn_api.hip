@@ -1,0 +1,120 @@
+// C ABI of the attention library: argument validation, then dispatch to the
+// kernel launchers.  Validation runs before anything is enqueued; on error no
+// work is launched and no output is touched.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+bool sizes_ok(int B, int H, int N) {
+  if (B <= 0 || H <= 0 || N <= 0) return false;
+  const int64_t rows = (int64_t)B * H * N;
+  return rows < ((int64_t)1 << 31);
+}
+
+bool scale_ok(float scale) { return std::isfinite(scale) && scale > 0.f; }
+
+attn_status_t map_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+attn_status_t check_bf16_d(int d, attn_dtype_t dtype) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                       int N, int d, attn_dtype_t dtype, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  return map_hip(attn::launch_fwd(q, k, v, o, lse, B * H, N, d, dtype == ATTN_BF16, scale, causal != 0,
+                                  (hipStream_t)stream));
+}
+
+namespace {
+size_t delta_bytes(int B, int H, int N) {
+  const size_t bytes = (size_t)B * H * N * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
+  (void)d;
+  if (!sizes_ok(B, H, N)) return 0;
+  return 2 * delta_bytes(B, H, N);  // approximate delta, then exact delta
+}
+
+attn_status_t attn_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int H, int N, int d,
+                                  attn_dtype_t dtype, void* stream) {
+  if (!o || !dout || !delta) return ATTN_ERR_INVALID;
+  if (!sizes_ok(B, H, N)) return ATTN_ERR_INVALID;
+  const attn_status_t s = check_bf16_d(d, dtype);
+  if (s != ATTN_OK) return s;
+  return map_hip(attn::launch_bwd_preprocess(o, dout, delta, B * H, N, d, (hipStream_t)stream));
+}
+
+attn_status_t attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                            const float* delta, void* dk, void* dv, int B, int H, int N, int d,
+                            attn_dtype_t dtype, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !lse || !dout || !delta || !dk || !dv) return ATTN_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  const attn_status_t s = check_bf16_d(d, dtype);
+  if (s != ATTN_OK) return s;
+  return map_hip(attn::launch_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, B * H, N, d, scale, causal != 0,
+                                       (hipStream_t)stream));
+}
+
+attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                          const float* delta, void* dq, float* delta_out, int B, int H, int N, int d,
+                          attn_dtype_t dtype, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !lse || !dout || !delta || !dq || !delta_out) return ATTN_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  const attn_status_t s = check_bf16_d(d, dtype);
+  if (s != ATTN_OK) return s;
+  return map_hip(attn::launch_bwd_dq(q, k, v, lse, dout, delta, dq, delta_out, B * H, N, d, scale,
+                                     causal != 0, (hipStream_t)stream));
+}
+
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                       size_t workspace_bytes, int B, int H, int N, int d, attn_dtype_t dtype, float scale,
+                       int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  const attn_status_t s = check_bf16_d(d, dtype);
+  if (s != ATTN_OK) return s;
+  if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d)) return ATTN_ERR_INVALID;
+  float* delta_approx = static_cast<float*>(workspace);
+  float* delta_exact = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes(B, H, N));
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = attn::launch_bwd_preprocess(o, dout, delta_approx, B * H, N, d, st);
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  e = attn::launch_bwd_dq(q, k, v, lse, dout, delta_approx, dq, delta_exact, B * H, N, d, scale, causal != 0,
+                          st);
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  e = attn::launch_bwd_dkdv(q, k, v, lse, dout, delta_exact, dk, dv, B * H, N, d, scale, causal != 0, st);
+  return map_hip(e);
+}
+
+const char* attn_status_string(attn_status_t s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
+    case ATTN_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+}  // extern "C"

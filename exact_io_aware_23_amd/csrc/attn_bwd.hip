@@ -1,0 +1,562 @@
+// Exact attention backward for gfx950: recompute P tile by tile from Q, K and
+// the saved row logsumexp L; never store an N x N array.
+//
+// The pages: "What is Flash Attention?" (iania.ai video page), transcript
+// 06:52-07:24: the forward keeps only O and per-row statistics, and the
+// backward rebuilds P block by block with the same tiling loop.  Transcript
+// 08:26: the gradients are those of the exact function.  The formulas below
+// are the calculus of O = softmax(S) V, S = scale Q K^T + mask (the pages do
+// not print them):
+//   P = exp(S - L)            (L_i = logsumexp of row i, saved by the forward)
+//   dV = P^T dO, dP = dO V^T, delta_i = sum_k dO_ik O_ik = sum_j P_ij dP_ij,
+//   dS = P * (dP - delta),   dQ = scale dS K,   dK = scale dS^T Q.
+//
+// Three kernels on one stream:
+//   preprocess : delta = rowsum(dO * O), fp32.
+//   dkdv       : a workgroup keeps 128 keys (32 per wave) of K and V in VGPRs
+//                and streams the 32-query blocks of Q and dO through LDS
+//                (row-major and transposed copies, both made from one global
+//                load).  Four MFMA products per block: S, dP, dV^T += dO^T P,
+//                dK^T += Q^T dS.  dK, dV accumulate in fp32 registers.
+//   dq         : a workgroup keeps 128 queries (32 per wave) of Q and dO in
+//                VGPRs and streams 64-key tiles of K, V and K^T through LDS.
+//                Four products per tile: S^T = K Q^T, dP^T = V dO^T,
+//                dQ^T += K^T dS~^T and (P K)^T += K^T P^T.  No atomics, so dQ
+//                is deterministic.
+// Precision of delta: rowsum(dO * O) with O rounded to bf16 differs from the
+// exact sum_j P_ij dP_ij by about 2^-9 |dO| |O|, and dP - delta cancels when a
+// row's P is nearly one-hot, so that error reaches dK and dQ almost unreduced.
+// The dq kernel therefore runs first: it forms dS~ = P (dP - delta~) with the
+// approximate delta~ (small after the cancellation, so its bf16 rounding is
+// harmless), accumulates the exact delta = sum_j P_ij dP_ij in fp32 on the way,
+// and adds the correction (delta~ - delta) (P K) at the end.  dkdv then uses
+// the exact delta.  Order: preprocess -> dq -> dkdv.
+// Both recompute P with p = exp2(s * scale * log2 e - L * log2 e).
+#include "attn_common.h"
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+__device__ __forceinline__ int t_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }  // 64-byte rows
+__device__ __forceinline__ int vt_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }   // 128-byte rows
+
+// ------------------------------------------------------------------ preprocess
+template <int D>
+__global__ void __launch_bounds__(256)
+bwd_preprocess_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO, float* __restrict__ delta,
+                      int rows) {
+  constexpr int TPR = D / 8;  // threads per row, 16 bytes each
+  const int row = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  float s = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(O + (size_t)row * D + 8 * part);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dO + (size_t)row * D + 8 * part);
+    const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+    const bf16x8 bv = __builtin_bit_cast(bf16x8, b);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = fmaf((float)av[i], (float)bv[i], s);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, TPR);
+  if (row < rows && part == 0) delta[row] = s;
+}
+
+// ------------------------------------------------------------------ dK, dV
+template <int D>
+struct DkdvCfg {
+  static constexpr int BKV = 128;  // keys per workgroup, 32 per wave
+  static constexpr int BQ = 32;    // queries per step
+  static constexpr int NCH = D / 8;
+  static constexpr int KS = D / 16;
+  static constexpr int DT = D / 32;
+  static constexpr int TILE = BQ * D;                      // bf16 elements of one Q or dO copy
+  static constexpr int STAGE_BYTES = 4 * TILE * 2 + 2 * BQ * 4;
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                const float* __restrict__ Lse, const bf16* __restrict__ dO, const float* __restrict__ Delta,
+                bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int n_ktiles, int total, float c,
+                float scale) {
+  using C = DkdvCfg<D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+
+  const int work = xcd_remap(blockIdx.x, total);
+  const int bh = work / n_ktiles;
+  const int kt = work % n_ktiles;
+  const size_t head = (size_t)bh * N * D;
+  const bf16* Qh = Q + head;
+  const bf16* dOh = dO + head;
+  const float* Lh = Lse + (size_t)bh * N;
+  const float* Dh = Delta + (size_t)bh * N;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int k0 = kt * C::BKV;
+  const int kw0 = k0 + 32 * wave;
+  const int key = kw0 + l32;
+
+  // ---- K^T and V^T operands (lane = key, 8 consecutive d per k-step)
+  bf16x8 kreg[C::KS], vreg[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    kreg[ks] = __builtin_bit_cast(bf16x8, gload16(K + head + (size_t)key * D + 16 * ks + 8 * g, key < N));
+    vreg[ks] = __builtin_bit_cast(bf16x8, gload16(V + head + (size_t)key * D + 16 * ks + 8 * g, key < N));
+  }
+
+  // ---- staging: thread -> (which tensor, 8 queries, 4 d columns)
+  const bool st_active = tid < 2 * D;
+  const int st_which = tid / D;           // 0: Q, 1: dO
+  const int st_local = tid % D;
+  const int st_qg = st_local & 3;         // queries 8*qg .. +7
+  const int st_dc = 4 * (st_local >> 2);  // d columns st_dc .. +3
+  const bf16* st_src = st_which ? dOh : Qh;
+  u32x2 stv[8];
+  float st_f = 0.f;
+
+  auto load_tile = [&](int q0) {
+    if (st_active) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int q = q0 + 8 * st_qg + e;
+        u32x2 z = {0u, 0u};
+        stv[e] = q < N ? *reinterpret_cast<const u32x2*>(st_src + (size_t)q * D + st_dc) : z;
+      }
+    }
+    if (tid < 64) {
+      const int q = q0 + (tid & 31);
+      if (tid < 32) st_f = q < N ? Lh[q] * kLog2e : INFINITY;
+      else st_f = q < N ? Dh[q] : 0.f;
+    }
+  };
+  auto store_tile = [&](int stage) {
+    char* base = smem + stage * C::STAGE_BYTES;
+    bf16* Xs = reinterpret_cast<bf16*>(base) + st_which * C::TILE;        // row-major copy
+    bf16* XTs = reinterpret_cast<bf16*>(base) + (2 + st_which) * C::TILE; // transposed copy
+    if (st_active) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int row = 8 * st_qg + e;
+        const int swz = swap23(row & 15) & (C::NCH - 1);
+        const int chunk = st_dc >> 3;
+        *reinterpret_cast<u32x2*>(Xs + row * D + 8 * (chunk ^ swz) + (st_dc & 7)) = stv[e];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int w = i >> 1;
+        u32x4 o;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          o[p] = (i & 1) ? pack_hi(stv[2 * p][w], stv[2 * p + 1][w]) : pack_lo(stv[2 * p][w], stv[2 * p + 1][w]);
+        const int row = st_dc + i;
+        lds_write16(XTs + row * C::BQ, st_qg ^ t_swz(row), o);
+      }
+    }
+    if (tid < 64) {
+      float* F = reinterpret_cast<float*>(base + 4 * C::TILE * 2);
+      F[tid] = st_f;  // Ls' at [0, 32), delta at [32, 64)
+    }
+  };
+
+  const int a_row = swap23(l32);
+  const int a_swz = (l32 & 15) & (C::NCH - 1);
+  const int tt_swz = t_swz(l32);
+
+  f32x16 dk[C::DT], dv[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[dt][r] = 0.f;
+      dv[dt][r] = 0.f;
+    }
+
+  const int n_qt = (N + C::BQ - 1) / C::BQ;
+  const int qt_begin = CAUSAL ? (k0 / C::BQ) : 0;
+
+  if (qt_begin < n_qt) {
+    load_tile(qt_begin * C::BQ);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = qt_begin; it < n_qt; ++it) {
+    const int stage = (it - qt_begin) & 1;
+    const int q0 = it * C::BQ;
+    const bool has_next = it + 1 < n_qt;
+    if (has_next) load_tile(q0 + C::BQ);
+
+    const bool active = kw0 < N && !(CAUSAL && q0 < kw0);
+    if (active) {
+      const char* base = smem + stage * C::STAGE_BYTES;
+      const bf16* Qs = reinterpret_cast<const bf16*>(base);
+      const bf16* dOs = Qs + C::TILE;
+      const bf16* QTs = Qs + 2 * C::TILE;
+      const bf16* dOTs = Qs + 3 * C::TILE;
+      const float* Ls = reinterpret_cast<const float*>(base + 4 * C::TILE * 2);
+      const float* Ds = Ls + 32;
+
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = 0.f;
+        dp[r] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8 aq = lds_read16(Qs + a_row * D, (2 * ks + g) ^ a_swz);
+        s = mfma32(aq, kreg[ks], s);
+        const bf16x8 ao = lds_read16(dOs + a_row * D, (2 * ks + g) ^ a_swz);
+        dp = mfma32(ao, vreg[ks], dp);
+      }
+      // per-register query statistics: query crow(r, g) = 16*(r/8) + 8*g + r%8
+      float lrow[16], drow[16];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v4 = 0; v4 < 2; ++v4) {
+          const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + 16 * h + 8 * g + 4 * v4);
+          const f32x4 dv4 = *reinterpret_cast<const f32x4*>(Ds + 16 * h + 8 * g + 4 * v4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            lrow[8 * h + 4 * v4 + i] = lv[i];
+            drow[8 * h + 4 * v4 + i] = dv4[i];
+          }
+        }
+      const bool need_mask = (kw0 + 32 > N) || (CAUSAL && q0 == kw0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(s[r], c, -lrow[r]));
+        if (need_mask) {
+          const int q = q0 + crow(r, g);
+          const bool bad = (key >= N) || (CAUSAL && key > q);
+          p = bad ? 0.f : p;
+        }
+        s[r] = p;
+        dp[r] = p * (dp[r] - drow[r]);
+      }
+      bf16x8 pop[2], dsop[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        pop[h] = c_to_operand(s, h);
+        dsop[h] = c_to_operand(dp, h);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const bf16x8 ado = lds_read16(dOTs + (32 * dt + l32) * C::BQ, (2 * h + g) ^ tt_swz);
+          dv[dt] = mfma32(ado, pop[h], dv[dt]);
+          const bf16x8 aqt = lds_read16(QTs + (32 * dt + l32) * C::BQ, (2 * h + g) ^ tt_swz);
+          dk[dt] = mfma32(aqt, dsop[h], dk[dt]);
+        }
+    }
+
+    if (has_next) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: dK = scale * dK^T^T, dV = dV^T^T
+  if (key < N) {
+    bf16* dKh = dK + head + (size_t)key * D;
+    bf16* dVh = dV + head + (size_t)key * D;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int dcol = 32 * dt + 8 * a + 4 * g;
+        u32x2 wk, wv;
+        wk[0] = pack_bf16x2(dk[dt][4 * a + 0] * scale, dk[dt][4 * a + 1] * scale);
+        wk[1] = pack_bf16x2(dk[dt][4 * a + 2] * scale, dk[dt][4 * a + 3] * scale);
+        wv[0] = pack_bf16x2(dv[dt][4 * a + 0], dv[dt][4 * a + 1]);
+        wv[1] = pack_bf16x2(dv[dt][4 * a + 2], dv[dt][4 * a + 3]);
+        *reinterpret_cast<u32x2*>(dKh + dcol) = wk;
+        *reinterpret_cast<u32x2*>(dVh + dcol) = wv;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+template <int D>
+struct DqCfg {
+  static constexpr int BRQ = 128;  // queries per workgroup, 32 per wave
+  static constexpr int BC = 64;    // keys per tile
+  static constexpr int NCH = D / 8;
+  static constexpr int KS = D / 16;
+  static constexpr int DT = D / 32;
+  static constexpr int DPT = D / 32;  // d columns per thread in the K transpose
+  static constexpr int NVLD = BC * NCH / 256;
+  static constexpr int TILE = BC * D;
+  static constexpr int STAGE = 3 * TILE;  // Ks, Vs, KTs
+};
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+              const float* __restrict__ Lse, const bf16* __restrict__ dO, const float* __restrict__ Delta,
+              bf16* __restrict__ dQ, float* __restrict__ DeltaOut, int N, int n_qtiles, int total, float c,
+              float scale) {
+  using C = DqCfg<D>;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
+
+  const int work = xcd_remap(blockIdx.x, total);
+  const int bh = work / n_qtiles;
+  const int qt = CAUSAL ? (n_qtiles - 1 - work % n_qtiles) : (work % n_qtiles);
+  const size_t head = (size_t)bh * N * D;
+  const bf16* Kh = K + head;
+  const bf16* Vh = V + head;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int q0w = qt * C::BRQ + 32 * wave;
+  const int q = q0w + l32;
+
+  bf16x8 qreg[C::KS], doreg[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    qreg[ks] = __builtin_bit_cast(bf16x8, gload16(Q + head + (size_t)q * D + 16 * ks + 8 * g, q < N));
+    doreg[ks] = __builtin_bit_cast(bf16x8, gload16(dO + head + (size_t)q * D + 16 * ks + 8 * g, q < N));
+  }
+  const float lq = q < N ? Lse[(size_t)bh * N + q] * kLog2e : INFINITY;
+  const float dq_delta = q < N ? Delta[(size_t)bh * N + q] : 0.f;  // approximate delta (from bf16 O)
+  float d_exact = 0.f;  // this lane's share of sum_j P_qj dP_qj
+
+  const int kv_end = CAUSAL ? min(N, qt * C::BRQ + C::BRQ) : N;
+  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  int wave_tiles = 0;
+  if (q0w < N) wave_tiles = CAUSAL ? (min(N, q0w + 32) + C::BC - 1) / C::BC : n_tiles;
+
+  // staging: V row-major with 16-byte loads; K with the transposing mapping
+  u32x4 vst[C::NVLD];
+  uint32_t kst[8][C::DPT / 2];
+  const int kkg = tid & 7;
+  const int kdg = tid >> 3;
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < C::NVLD; ++i) {
+      const int idx = tid + 256 * i;
+      const int row = idx / C::NCH, ch = idx % C::NCH;
+      const int key = kv0 + row;
+      vst[i] = gload16(Vh + (size_t)key * D + 8 * ch, key < N);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = kv0 + 8 * kkg + e;
+      const bf16* p = Kh + (size_t)key * D + C::DPT * kdg;
+      if constexpr (C::DPT == 4) {
+        u32x2 z = {0u, 0u};
+        u32x2 x = key < N ? *reinterpret_cast<const u32x2*>(p) : z;
+        kst[e][0] = x[0];
+        kst[e][1] = x[1];
+      } else {
+        kst[e][0] = key < N ? *reinterpret_cast<const uint32_t*>(p) : 0u;
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+    bf16* Ks = smem + stage * C::STAGE;
+    bf16* Vs = Ks + C::TILE;
+    bf16* KTs = Ks + 2 * C::TILE;
+#pragma unroll
+    for (int i = 0; i < C::NVLD; ++i) {
+      const int idx = tid + 256 * i;
+      const int row = idx / C::NCH, ch = idx % C::NCH;
+      lds_write16(Vs + row * D, ch ^ (swap23(row & 15) & (C::NCH - 1)), vst[i]);
+    }
+    const int dcol0 = C::DPT * kdg;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int row = 8 * kkg + e;
+      const int swz = swap23(row & 15) & (C::NCH - 1);
+      bf16* dst = Ks + row * D + 8 * ((dcol0 >> 3) ^ swz) + (dcol0 & 7);
+      if constexpr (C::DPT == 4) {
+        u32x2 x;
+        x[0] = kst[e][0];
+        x[1] = kst[e][1];
+        *reinterpret_cast<u32x2*>(dst) = x;
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = kst[e][0];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::DPT; ++i) {
+      const int w = i >> 1;
+      u32x4 o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        o[p] = (i & 1) ? pack_hi(kst[2 * p][w], kst[2 * p + 1][w]) : pack_lo(kst[2 * p][w], kst[2 * p + 1][w]);
+      const int row = dcol0 + i;
+      lds_write16(KTs + row * C::BC, kkg ^ vt_swz(row), o);
+    }
+  };
+
+  const int a_row = swap23(l32);
+  const int a_swz = (l32 & 15) & (C::NCH - 1);
+  const int v_swz = vt_swz(l32);
+
+  f32x16 dq[C::DT], pk[C::DT];  // dQ^T with the approximate delta, and (P K)^T
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dq[dt][r] = 0.f;
+      pk[dt][r] = 0.f;
+    }
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int stage = j & 1;
+    const int kv0 = j * C::BC;
+    const bool has_next = j + 1 < n_tiles;
+    if (has_next) load_tile(kv0 + C::BC);
+
+    if (j < wave_tiles) {
+      const bf16* Ks = smem + stage * C::STAGE;
+      const bf16* Vs = Ks + C::TILE;
+      const bf16* KTs = Ks + 2 * C::TILE;
+      f32x16 st[2], dpt[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          st[kb][r] = 0.f;
+          dpt[kb][r] = 0.f;
+        }
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 ak = lds_read16(Ks + (32 * kb + a_row) * D, (2 * ks + g) ^ a_swz);
+          st[kb] = mfma32(ak, qreg[ks], st[kb]);
+          const bf16x8 av = lds_read16(Vs + (32 * kb + a_row) * D, (2 * ks + g) ^ a_swz);
+          dpt[kb] = mfma32(av, doreg[ks], dpt[kb]);
+        }
+      const bool need_mask = (kv0 + C::BC > N) || (CAUSAL && kv0 + C::BC - 1 > q0w);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(fmaf(st[kb][r], c, -lq));
+          if (need_mask) {
+            const int key = kv0 + 32 * kb + crow(r, g);
+            const bool bad = (key >= N) || (CAUSAL && key > q);
+            p = bad ? 0.f : p;
+          }
+          d_exact = fmaf(p, dpt[kb][r], d_exact);
+          dpt[kb][r] = p * (dpt[kb][r] - dq_delta);
+          st[kb][r] = p;
+        }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const bf16x8 dso = c_to_operand(dpt[m >> 1], m & 1);
+        const bf16x8 po = c_to_operand(st[m >> 1], m & 1);
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const bf16x8 akt = lds_read16(KTs + (32 * dt + l32) * C::BC, (2 * m + g) ^ v_swz);
+          dq[dt] = mfma32(akt, dso, dq[dt]);
+          pk[dt] = mfma32(akt, po, pk[dt]);
+        }
+      }
+    }
+
+    if (has_next) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // exact delta_q = sum_j P_qj dP_qj; dS was formed with the approximate delta,
+  // so dQ = scale * (dS~ K + (delta~ - delta) P K)
+  d_exact = pair_sum(d_exact);
+  const float corr = dq_delta - d_exact;
+  if (q < N) {
+    bf16* dQh = dQ + head + (size_t)q * D;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int dcol = 32 * dt + 8 * a + 4 * g;
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = scale * fmaf(corr, pk[dt][4 * a + i], dq[dt][4 * a + i]);
+        u32x2 w;
+        w[0] = pack_bf16x2(v[0], v[1]);
+        w[1] = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<u32x2*>(dQh + dcol) = w;
+      }
+    if (g == 0) DeltaOut[(size_t)bh * N + q] = d_exact;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                         const float* delta, void* dk, void* dv, int BH, int N, float scale,
+                         hipStream_t stream) {
+  using C = DkdvCfg<D>;
+  const int n_kt = (N + C::BKV - 1) / C::BKV;
+  const int total = BH * n_kt;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, stream, (const bf16*)q,
+                     (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dk, (bf16*)dv, N,
+                     n_kt, total, scale * kLog2e, scale);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dq_t(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                       const float* delta, void* dq, float* delta_out, int BH, int N, float scale,
+                       hipStream_t stream) {
+  using C = DqCfg<D>;
+  const int n_qt = (N + C::BRQ - 1) / C::BRQ;
+  const int total = BH * n_qt;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, stream, (const bf16*)q,
+                     (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dq, delta_out, N, n_qt, total,
+                     scale * kLog2e, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int BH, int N, int d,
+                                 hipStream_t stream) {
+  const int rows = BH * N;
+  if (d == 64) {
+    hipLaunchKernelGGL((bwd_preprocess_kernel<64>), dim3((rows + 31) / 32), dim3(256), 0, stream,
+                       (const bf16*)o, (const bf16*)dout, delta, rows);
+  } else {
+    hipLaunchKernelGGL((bwd_preprocess_kernel<128>), dim3((rows + 15) / 16), dim3(256), 0, stream,
+                       (const bf16*)o, (const bf16*)dout, delta, rows);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                           const float* delta, void* dk, void* dv, int BH, int N, int d, float scale,
+                           bool causal, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_dkdv_t<64, true>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, stream)
+                  : launch_dkdv_t<64, false>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, stream);
+  return causal ? launch_dkdv_t<128, true>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, stream)
+                : launch_dkdv_t<128, false>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, stream);
+}
+
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                         const float* delta, void* dq, float* delta_out, int BH, int N, int d, float scale,
+                         bool causal, hipStream_t stream) {
+  if (d == 64)
+    return causal ? launch_dq_t<64, true>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, stream)
+                  : launch_dq_t<64, false>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, stream);
+  return causal ? launch_dq_t<128, true>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, stream)
+                : launch_dq_t<128, false>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, stream);
+}
+
+}  // namespace attn

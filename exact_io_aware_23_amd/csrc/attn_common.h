@@ -1,0 +1,106 @@
+// Device-side building blocks shared by the attention kernels (gfx950 only).
+//
+// Matrix-core conventions (v_mfma_f32_32x32x16_bf16, wave64), checked on the
+// hardware:
+//   A operand (32 x 16): lane l holds A[l % 32][8 * (l / 32) + e], e = 0..7
+//   B operand (16 x 32): lane l holds B[8 * (l / 32) + e][l % 32]
+//   C/D       (32 x 32): lane l, register r holds C[8*(r/4) + 4*(l/32) + r%4][l % 32]
+// Only the pairing of A's and B's k slots matters for the product, so any
+// consistent assignment of the contraction index to (l / 32, e) is valid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// max over the lane pair (l, l ^ 32): v_permlane32_swap gives each lane both halves
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Swap bits 2 and 3 of a lane/row index.  Reading operand rows in this order
+// makes the C registers of a 32x32 tile line up with 8 consecutive indices per
+// lane half when they are reused as the k operand of the next product.
+__device__ __forceinline__ int swap23(int i) {
+  return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
+}
+
+// Row index (within a 32-row tile whose A-operand rows were read in swap23
+// order) held by C register r in lane half g:
+//   swap23(8*(r/4) + 4*g + r%4) = 16*(r/8) + 8*g + r%8
+__device__ __forceinline__ constexpr int crow(int r, int g) { return 16 * (r / 8) + 8 * g + (r % 8); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16 a = (bf16)lo, b = (bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Eight consecutive C registers [8h, 8h+8) of a 32x32 fp32 tile, as a bf16x8
+// operand (the k = 8 * (l/32) + e slots of the next product).
+__device__ __forceinline__ bf16x8 c_to_operand(const f32x16& c, int h) {
+  u32x4 u;
+  u[0] = pack_bf16x2(c[8 * h + 0], c[8 * h + 1]);
+  u[1] = pack_bf16x2(c[8 * h + 2], c[8 * h + 3]);
+  u[2] = pack_bf16x2(c[8 * h + 4], c[8 * h + 5]);
+  u[3] = pack_bf16x2(c[8 * h + 6], c[8 * h + 7]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// LDS access helpers (16-byte granularity)
+__device__ __forceinline__ bf16x8 lds_read16(const bf16* base, int chunk16) {
+  return *reinterpret_cast<const bf16x8*>(base + 8 * chunk16);
+}
+__device__ __forceinline__ void lds_write16(bf16* base, int chunk16, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(base + 8 * chunk16) = v;
+}
+
+// 16-byte global load with zero fill when !valid
+__device__ __forceinline__ u32x4 gload16(const bf16* p, bool valid) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return valid ? *reinterpret_cast<const u32x4*>(p) : z;
+}
+
+// Select the 16-bit half `half` (0 = low) of two dwords and pack them: low from
+// a, high from b.  Used to transpose 2x2 blocks of bf16 pairs in registers.
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);  // [a.lo, b.lo]
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);  // [a.hi, b.hi]
+}
+
+// XCD-aware work index.  Workgroups are handed to the 8 XCDs round-robin by
+// linear id; renumbering so that each XCD walks a contiguous range of work
+// items keeps the tiles of one head (which share K/V, or Q/dO) in one L2.
+__device__ __forceinline__ int xcd_remap(int wid, int total) {
+  if ((total & 7) != 0) return wid;
+  return (wid & 7) * (total >> 3) + (wid >> 3);
+}
+
+}  // namespace attn

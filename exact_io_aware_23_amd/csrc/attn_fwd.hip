@@ -1,0 +1,389 @@
+// Fused exact attention forward for gfx950.
+//
+// What it computes (the pages, by title and section):
+//   "What is Flash Attention?" (iania.ai video page), transcript 01:04: S = Q K^T
+//   scaled, row softmax P, O = P V.  Transcript 02:38-03:44: one kernel, one Q
+//   block kept on chip while K/V blocks stream through, only O written.
+//   Transcript 04:15-05:17: the online softmax with a running max m and sum l,
+//   the accumulator rescaled as each block arrives, and one division by l at
+//   the end.  "Atencao exata ..." (mentria.ai), online-update formula: the
+//   single-exponential form l_new = e^(m_old - m_new) l_old + sum e^(x - m_new)
+//   used here.
+//
+// bf16 kernel design (MI355X, CDNA4):
+//   * One workgroup = 4 waves = 256 query rows; each wave owns 64 query rows as
+//     two 32-row blocks so every K or V^T fragment read from LDS feeds two MFMAs.
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T kept in
+//     VGPRs for the whole loop).  In the S^T layout each lane owns one query
+//     row, so the row max, the exp-sum and the O rescale stay lane-local; one
+//     v_permlane32_swap joins the two lane halves for the max.
+//   * O^T += V^T P^T: P^T comes straight from the S^T accumulators (rounded to
+//     bf16), V^T fragments from LDS.  V is transposed in registers while it is
+//     staged, so every LDS operand read is a conflict-free ds_read_b128.
+//   * Softmax in base 2: p = exp2(s * scale * log2(e) - m) with one FMA and one
+//     v_exp_f32 per score; L = (m + log2 l) ln 2 at the end.
+//   * K/V tiles of 64 keys are double-buffered in LDS; the global loads of
+//     tile j+1 are in flight while tile j is computed.  One barrier per tile.
+//   * Causal: key tiles past a query tile's last row are never loaded; a wave
+//     skips the tiles past its own last row; only diagonal (and ragged tail)
+//     tiles apply the mask.  Query tiles run longest first within a head, and
+//     work items are renumbered so each XCD sweeps whole heads (L2 reuse).
+#include "attn_common.h"
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+template <int D>
+struct FwdCfg {
+  static constexpr int WAVES = 4;
+  static constexpr int QB = 2;               // 32-row query blocks per wave
+  static constexpr int BR = WAVES * QB * 32; // 256 query rows per workgroup
+  static constexpr int BC = 64;              // keys per K/V tile
+  static constexpr int NCH = D / 8;          // 16-byte chunks per K row
+  static constexpr int KS = D / 16;          // k-steps of S^T = K Q^T
+  static constexpr int DT = D / 32;          // 32-wide d tiles of O^T
+  static constexpr int DPT = D / 32;         // d columns per thread in the V transpose
+  static constexpr int NKLD = BC * NCH / 256;
+  static constexpr int K_ELEMS = BC * D;
+  static constexpr int STAGE = 2 * BC * D;   // K and V^T
+};
+
+__device__ __forceinline__ int vt_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1)
+fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                bf16* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, int total, float c) {
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
+
+  const int work = xcd_remap(blockIdx.x, total);
+  const int bh = work / n_qtiles;
+  const int qt = CAUSAL ? (n_qtiles - 1 - work % n_qtiles) : (work % n_qtiles);
+  const size_t head = (size_t)bh * N * D;
+  const bf16* Qh = Q + head;
+  const bf16* Kh = K + head;
+  const bf16* Vh = V + head;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int q0w = qt * C::BR + wave * (C::QB * 32);
+
+  // ---- tile ranges
+  const int kv_end = CAUSAL ? min(N, qt * C::BR + C::BR) : N;
+  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  int wave_tiles = 0;
+  if (q0w < N) {
+    const int wend = CAUSAL ? min(N, q0w + C::QB * 32) : N;
+    wave_tiles = (wend + C::BC - 1) / C::BC;
+  }
+
+  // ---- Q^T operand in registers: lane (l32, g) holds Q[q][16ks + 8g .. +7]
+  bf16x8 qreg[C::QB][C::KS];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int q = q0w + 32 * qb + l32;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 v = gload16(Qh + (size_t)q * D + 16 * ks + 8 * g, q < N);
+      qreg[qb][ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // ---- staging helpers
+  u32x4 kst[C::NKLD];
+  uint32_t vst[8][C::DPT / 2];
+  const int vkg = tid & 7;   // key group (8 keys) in the V transpose
+  const int vdg = tid >> 3;  // d group (DPT columns)
+
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int i = 0; i < C::NKLD; ++i) {
+      const int idx = tid + 256 * i;
+      const int row = idx / C::NCH, ch = idx % C::NCH;
+      const int key = kv0 + row;
+      kst[i] = gload16(Kh + (size_t)key * D + 8 * ch, key < N);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = kv0 + 8 * vkg + e;
+      const bf16* p = Vh + (size_t)key * D + C::DPT * vdg;
+      if constexpr (C::DPT == 4) {
+        u32x2 z = {0u, 0u};
+        u32x2 x = key < N ? *reinterpret_cast<const u32x2*>(p) : z;
+        vst[e][0] = x[0];
+        vst[e][1] = x[1];
+      } else {
+        vst[e][0] = key < N ? *reinterpret_cast<const uint32_t*>(p) : 0u;
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+    bf16* Ks = smem + stage * C::STAGE;
+    bf16* Vts = Ks + C::K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < C::NKLD; ++i) {
+      const int idx = tid + 256 * i;
+      const int row = idx / C::NCH, ch = idx % C::NCH;
+      const int swz = swap23(row & 15) & (C::NCH - 1);
+      lds_write16(Ks + row * D, ch ^ swz, kst[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < C::DPT; ++i) {
+      const int w = i >> 1;
+      u32x4 o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        o[p] = (i & 1) ? pack_hi(vst[2 * p][w], vst[2 * p + 1][w]) : pack_lo(vst[2 * p][w], vst[2 * p + 1][w]);
+      const int row = C::DPT * vdg + i;
+      lds_write16(Vts + row * C::BC, vkg ^ vt_swz(row), o);
+    }
+  };
+
+  // per-lane LDS read offsets
+  const int k_swz = (l32 & 15) & (C::NCH - 1);
+  const int krow = swap23(l32);
+  const int v_swz = vt_swz(l32);
+
+  f32x16 oacc[C::QB][C::DT];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qb][dt][r] = 0.f;
+  float m_run[C::QB], l_run[C::QB];
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    m_run[qb] = -1e30f;
+    l_run[qb] = 0.f;
+  }
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int stage = j & 1;
+    const int kv0 = j * C::BC;
+    const bool has_next = j + 1 < n_tiles;
+    if (has_next) load_tile(kv0 + C::BC);
+
+    if (j < wave_tiles) {
+      const bf16* Ks = smem + stage * C::STAGE;
+      const bf16* Vts = Ks + C::K_ELEMS;
+      // ---- S^T = K Q^T
+      f32x16 st[C::QB][2];
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st[qb][kb][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 a = lds_read16(Ks + (32 * kb + krow) * D, (2 * ks + g) ^ k_swz);
+#pragma unroll
+          for (int qb = 0; qb < C::QB; ++qb) st[qb][kb] = mfma32(a, qreg[qb][ks], st[qb][kb]);
+        }
+      }
+      // ---- mask (diagonal / ragged tiles only)
+      const bool need_mask = (kv0 + C::BC > N) || (CAUSAL && kv0 + C::BC - 1 > q0w);
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < C::QB; ++qb) {
+          const int q = q0w + 32 * qb + l32;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = kv0 + 32 * kb + crow(r, g);
+              const bool bad = (key >= N) || (CAUSAL && key > q);
+              st[qb][kb][r] = bad ? -INFINITY : st[qb][kb][r];
+            }
+        }
+      }
+      // ---- online softmax (base 2), lane-local per query row
+      bf16x8 pop[C::QB][4];
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[qb][kb][r]);
+        mx = pair_max(mx);
+        const float m_new = fmaxf(m_run[qb], mx * c);
+        const float alpha = fast_exp2(m_run[qb] - m_new);
+        m_run[qb] = m_new;
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(st[qb][kb][r], c, -m_new));
+            st[qb][kb][r] = p;
+            rs += p;
+          }
+        l_run[qb] = l_run[qb] * alpha + rs;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qb][dt][r] *= alpha;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) pop[qb][m] = c_to_operand(st[qb][m >> 1], m & 1);
+      }
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const bf16x8 a = lds_read16(Vts + (32 * dt + l32) * C::BC, (2 * m + g) ^ v_swz);
+#pragma unroll
+          for (int qb = 0; qb < C::QB; ++qb) oacc[qb][dt] = mfma32(a, pop[qb][m], oacc[qb][dt]);
+        }
+      }
+    }
+
+    if (has_next) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O_acc / l, L = (m + log2 l) ln 2
+  bf16* Oh = O + head;
+  float* Lh = L + (size_t)bh * N;
+#pragma unroll
+  for (int qb = 0; qb < C::QB; ++qb) {
+    const int q = q0w + 32 * qb + l32;
+    const float lt = pair_sum(l_run[qb]);
+    if (q < N) {
+      const float inv = 1.0f / lt;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const int dcol = 32 * dt + 8 * a + 4 * g;
+          u32x2 w;
+          w[0] = pack_bf16x2(oacc[qb][dt][4 * a + 0] * inv, oacc[qb][dt][4 * a + 1] * inv);
+          w[1] = pack_bf16x2(oacc[qb][dt][4 * a + 2] * inv, oacc[qb][dt][4 * a + 3] * inv);
+          *reinterpret_cast<u32x2*>(Oh + (size_t)q * D + dcol) = w;
+        }
+      if (g == 0) Lh[q] = (m_run[qb] + log2f(lt)) * kLn2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 forward: the same online-softmax algorithm on plain fp32 VALU
+// arithmetic.  One thread owns one query row (q and the O accumulator in
+// VGPRs); 32-key K/V tiles are staged in LDS and read as broadcasts.
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(64)
+fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+               float* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, float c) {
+  constexpr int BC = 32;
+  __shared__ float Ks[BC][D];
+  __shared__ float Vs[BC][D];
+  const int bh = blockIdx.x / n_qtiles;
+  const int qt = blockIdx.x % n_qtiles;
+  const size_t head = (size_t)bh * N * D;
+  const int q = qt * 64 + threadIdx.x;
+  const bool qv = q < N;
+
+  float qr[D], acc[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    qr[i] = qv ? Q[head + (size_t)q * D + i] : 0.f;
+    acc[i] = 0.f;
+  }
+  float m_run = -1e30f, l_run = 0.f;
+  const int kv_end = CAUSAL ? min(N, qt * 64 + 64) : N;
+  for (int kv0 = 0; kv0 < kv_end; kv0 += BC) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < BC * D; idx += 64) {
+      const int row = idx / D, col = idx % D;
+      const int key = kv0 + row;
+      Ks[row][col] = key < N ? K[head + (size_t)key * D + col] : 0.f;
+      Vs[row][col] = key < N ? V[head + (size_t)key * D + col] : 0.f;
+    }
+    __syncthreads();
+    float s[BC];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < BC; ++j) {
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) dot = fmaf(qr[i], Ks[j][i], dot);
+      const int key = kv0 + j;
+      const bool bad = key >= N || (CAUSAL && key > q);
+      s[j] = bad ? -INFINITY : dot;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m_run, mx * c);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) acc[i] *= alpha;
+#pragma unroll
+    for (int j = 0; j < BC; ++j) {
+      const float p = exp2f(fmaf(s[j], c, -m_new));
+      rs += p;
+#pragma unroll
+      for (int i = 0; i < D; ++i) acc[i] = fmaf(p, Vs[j][i], acc[i]);
+    }
+    l_run = l_run * alpha + rs;
+  }
+  if (qv) {
+    const float inv = 1.0f / l_run;
+#pragma unroll
+    for (int i = 0; i < D; ++i) O[head + (size_t)q * D + i] = acc[i] * inv;
+    L[(size_t)bh * N + q] = (m_run + log2f(l_run)) * kLn2;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                             int N, float scale, hipStream_t stream) {
+  using C = FwdCfg<D>;
+  const int n_qtiles = (N + C::BR - 1) / C::BR;
+  const int total = BH * n_qtiles;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, stream,
+                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
+                     scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_fwd_f32_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                            int N, float scale, hipStream_t stream) {
+  const int n_qtiles = (N + 63) / 64;
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(BH * n_qtiles), dim3(64), 0, stream,
+                     (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, N, n_qtiles,
+                     scale * kLog2e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
+                      int d, bool bf16_in, float scale, bool causal, hipStream_t stream) {
+  if (bf16_in) {
+    if (d == 64) return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, BH, N, scale, stream)
+                               : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, BH, N, scale, stream);
+    return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, stream)
+                  : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, stream);
+  }
+  if (d == 64) return causal ? launch_fwd_f32_t<64, true>(q, k, v, o, lse, BH, N, scale, stream)
+                             : launch_fwd_f32_t<64, false>(q, k, v, o, lse, BH, N, scale, stream);
+  return causal ? launch_fwd_f32_t<128, true>(q, k, v, o, lse, BH, N, scale, stream)
+                : launch_fwd_f32_t<128, false>(q, k, v, o, lse, BH, N, scale, stream);
+}
+
+}  // namespace attn

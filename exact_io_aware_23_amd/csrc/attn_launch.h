@@ -1,0 +1,22 @@
+// Internal launchers behind the C ABI.  Arguments are already validated;
+// BH = B * H.  Each returns hipGetLastError() after enqueueing on `stream`.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace attn {
+
+hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
+                      int d, bool bf16_in, float scale, bool causal, hipStream_t stream);
+
+hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int BH, int N, int d,
+                                 hipStream_t stream);
+
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                           const void* dout, const float* delta, void* dk, void* dv, int BH, int N,
+                           int d, float scale, bool causal, hipStream_t stream);
+
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                         const void* dout, const float* delta, void* dq, float* delta_out, int BH, int N,
+                         int d, float scale, bool causal, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,132 @@
+/*
+ * attn.h - C ABI of the exact fused attention library for AMD MI355X (gfx950).
+ *
+ * The library computes exact scaled-dot-product attention
+ *     O = softmax(scale * Q K^T + mask) V
+ * per (batch, head) pair.  Sources for the operation (the pages, by title):
+ *   - "What is Flash Attention?" (iania.ai video page), transcript 01:04:
+ *     scores S = Q K^T / sqrt(D), row softmax P, output O = P V.
+ *   - Same page, transcript 02:38-05:17: one fused kernel, Q kept on chip,
+ *     K/V visited in blocks, online softmax with a running max and sum.
+ *   - Same page, transcript 06:52-07:24: the backward keeps O and a small
+ *     per-row statistic and recomputes P block by block.
+ *   - "Atencao exata, acelerada por nunca escrever a grade gigante"
+ *     (mentria.ai): block scores, safe softmax, online update, o_flash = o_exact.
+ * The N x N score and probability matrices are never stored in device memory.
+ *
+ * Conventions shared by every entry point:
+ *   - Q, K, V, O, dO, dQ, dK, dV are dense row-major [B, H, N, d] arrays
+ *     (d fastest), all with the same B, H, N, d.  Pointers are device pointers
+ *     aligned to at least 16 bytes.  `dtype` gives their element type.
+ *   - lse (the per-row logsumexp L_i = m_i + ln l_i of the scaled, masked
+ *     scores, natural log) and delta (D_i = sum_k dO_ik O_ik) are fp32 [B, H, N].
+ *   - causal = 1 lets query i attend keys j <= i (square, top-left aligned);
+ *     causal = 0 attends all N keys.
+ *   - scale must be finite and > 0 (usually 1/sqrt(d)).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; it never synchronises.  The caller owns
+ *     all buffers and keeps them alive until the stream has passed the work.
+ *   - The library allocates no device memory and keeps no global state; calls
+ *     on different streams may run concurrently.
+ *   - Validation happens before anything is enqueued.  On any error nothing is
+ *     launched and no output is written.  ATTN_OK means "enqueued"; a device
+ *     fault shows up at the caller's next synchronisation.
+ *   - Supported: dtype ATTN_BF16 with d in {64, 128} for every entry point;
+ *     dtype ATTN_F32 with d in {64, 128} for attn_fwd only.  N >= 1 (any N,
+ *     not only multiples of the tile size), B, H >= 1, B*H*N < 2^31.
+ */
+#ifndef EXACT_ATTN_H
+#define EXACT_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = 1,     /* null pointer, non-positive size, bad scale/causal, workspace too small */
+  ATTN_ERR_UNSUPPORTED = 2, /* d or dtype outside the supported set */
+  ATTN_ERR_HIP = 3          /* the HIP runtime refused a launch */
+} attn_status_t;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
+
+/* Forward pass: O = softmax(scale Q K^T + mask) V and L = logsumexp of each
+ * row of scale Q K^T + mask.  One fused kernel; per query tile it streams the
+ * K/V blocks through on-chip memory with the online softmax (video page,
+ * transcript 03:44-05:17; slides, online-update formula).
+ *   q, k, v : inputs [B,H,N,d] of `dtype`.
+ *   o       : output [B,H,N,d] of `dtype` (rounded to nearest even for bf16).
+ *   lse     : output [B,H,N] fp32.  Must not alias any input. */
+attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int N, int d, attn_dtype_t dtype, float scale, int causal,
+                       void* stream);
+
+/* Bytes of device workspace attn_bwd needs: two fp32 [B,H,N] arrays (the
+ * approximate and the exact delta), each B*H*N*4 bytes rounded up to 256.
+ * Pure host arithmetic; returns 0 for invalid sizes. */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Backward pass: gradients of O with respect to Q, K and V for an upstream
+ * gradient dO, given the forward's O and L.  P is recomputed tile by tile from
+ * Q, K and L (video page, transcript 06:52-07:24); no N x N array is stored.
+ * Enqueues attn_bwd_preprocess, attn_bwd_dq and attn_bwd_dkdv in that order;
+ * the dq stage hands the exact delta to the dkdv stage through the workspace.
+ *   q, k, v, o, dout : inputs [B,H,N,d] of `dtype`; lse : input [B,H,N] fp32
+ *   dq, dk, dv       : outputs [B,H,N,d] of `dtype`
+ *   workspace        : device buffer of at least attn_bwd_workspace_bytes(...)
+ *                      bytes, holding delta; its contents on entry are ignored. */
+attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                       attn_dtype_t dtype, float scale, int causal, void* stream);
+
+/* Backward stage 1: delta~_i = sum_k dO_ik * O_ik in fp32.  Mathematically
+ * equal to sum_j P_ij dP_ij (the row term of the softmax Jacobian); with O
+ * rounded to bf16 it is an approximation that stage 2 refines.
+ *   o, dout : inputs [B,H,N,d] of `dtype`; delta : output [B,H,N] fp32. */
+attn_status_t attn_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int H,
+                                  int N, int d, attn_dtype_t dtype, void* stream);
+
+/* Backward stage 3: dK and dV.  One workgroup per block of keys keeps K and V
+ * on chip and visits the query blocks, recomputing S = scale Q K^T and
+ * P = exp(S - L) per block, then dV += P^T dO, dP = dO V^T,
+ * dS = P (dP - delta), dK += scale dS^T Q.
+ *   q, k, v, dout : inputs of `dtype`; lse, delta : fp32 inputs [B,H,N]
+ *                   (delta: the exact one written by attn_bwd_dq)
+ *   dk, dv        : outputs [B,H,N,d] of `dtype`. */
+attn_status_t attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                            const void* dout, const float* delta, void* dk, void* dv, int B,
+                            int H, int N, int d, attn_dtype_t dtype, float scale, int causal,
+                            void* stream);
+
+/* Backward stage 2: dQ and the exact delta.  One workgroup per block of
+ * queries keeps Q and dO on chip and visits the key blocks, recomputing
+ * P = exp(S - L) and dP = dO V^T per block.  It forms dS~ = P (dP - delta~)
+ * with the approximate delta~ from stage 1, accumulates
+ * delta_i = sum_j P_ij dP_ij in fp32 as it goes, and returns
+ * dQ = scale (dS~ K + (delta~ - delta) P K), which equals scale dS K with the
+ * exact delta.  No atomics: the result is deterministic.
+ *   q, k, v, dout : inputs of `dtype`; lse, delta : fp32 inputs [B,H,N]
+ *   dq            : output [B,H,N,d] of `dtype`
+ *   delta_out     : output [B,H,N] fp32, the exact delta (may not alias delta). */
+attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                          const void* dout, const float* delta, void* dq, float* delta_out, int B,
+                          int H, int N, int d, attn_dtype_t dtype, float scale, int causal,
+                          void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* attn_status_string(attn_status_t s);
+
+/* ATTN_ABI_VERSION of the built library. */
+int attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTN_H */

@@ -1,0 +1,120 @@
+"""The C ABI library: it loads, exports every declared entry point, and rejects
+bad arguments before touching the GPU (these calls never launch a kernel, so
+they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_io_aware_23_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from exact_io_aware_23_amd.build import build
+
+        build()
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted([
+        "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess", "attn_bwd_dkdv",
+        "attn_bwd_dq", "attn_status_string", "attn_abi_version"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # and as plain C symbols (no C++ mangling)
+    out = os.popen(f"nm -D --defined-only {binding.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define ATTN_ABI_VERSION (\d+)", open(HEADER).read())
+    assert lib.attn_abi_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for s in range(4):
+        assert lib.attn_status_string(s)
+    assert lib.attn_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    assert lib.attn_bwd_workspace_bytes(2, 32, 8192, 128) == 2 * (2 * 32 * 8192 * 4)
+    assert lib.attn_bwd_workspace_bytes(1, 1, 3, 64) == 512
+    assert lib.attn_bwd_workspace_bytes(0, 1, 3, 64) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 1, -1, 64) == 0
+
+
+def fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, dtype=1, scale=0.125, causal=0):
+    return lib.attn_fwd(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, None)
+
+
+def test_fwd_validation(lib):
+    INV, UNS = binding.ATTN_ERR_INVALID, binding.ATTN_ERR_UNSUPPORTED
+    for kw in ("q", "k", "v", "o", "lse"):
+        assert fwd(lib, **{kw: None}) == INV
+    assert fwd(lib, B=0) == INV
+    assert fwd(lib, H=-1) == INV
+    assert fwd(lib, N=0) == INV
+    assert fwd(lib, B=1 << 16, H=1 << 16, N=1) == INV  # B*H*N >= 2^31
+    assert fwd(lib, scale=0.0) == INV
+    assert fwd(lib, scale=-1.0) == INV
+    assert fwd(lib, scale=float("nan")) == INV
+    assert fwd(lib, scale=float("inf")) == INV
+    assert fwd(lib, causal=2) == INV
+    assert fwd(lib, d=96) == UNS
+    assert fwd(lib, d=256) == UNS
+    assert fwd(lib, dtype=7) == UNS
+
+
+def test_bwd_validation(lib):
+    INV, UNS = binding.ATTN_ERR_INVALID, binding.ATTN_ERR_UNSUPPORTED
+    ws = lib.attn_bwd_workspace_bytes(1, 2, 100, 64)
+
+    def bwd(ptrs=None, ws_bytes=ws, B=1, H=2, N=100, d=64, dtype=1, scale=0.125, causal=1):
+        p = ptrs or [FAKE] * 10
+        return lib.attn_bwd(*p, ws_bytes, B, H, N, d, dtype, scale, causal, None)
+
+    for i in range(10):
+        p = [FAKE] * 10
+        p[i] = None
+        assert bwd(p) == INV, i
+    assert bwd(ws_bytes=ws - 1) == INV
+    assert bwd(N=0) == INV
+    assert bwd(scale=-0.5) == INV
+    assert bwd(causal=-1) == INV
+    assert bwd(d=32) == UNS
+    assert bwd(dtype=0) == UNS  # fp32 backward is not provided
+    assert lib.attn_bwd_preprocess(FAKE, FAKE, None, 1, 1, 8, 64, 1, None) == INV
+    assert lib.attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 1, 8, 80, 1, None) == UNS
+    assert lib.attn_bwd_dkdv(*([FAKE] * 7), None, 1, 1, 8, 64, 1, 0.1, 0, None) == INV
+    assert lib.attn_bwd_dkdv(*([FAKE] * 8), 1, 1, 8, 64, 0, 0.1, 0, None) == UNS
+    assert lib.attn_bwd_dq(*([FAKE] * 6), None, FAKE, 1, 1, 8, 64, 1, 0.1, 0, None) == INV
+    assert lib.attn_bwd_dq(*([FAKE] * 7), None, 1, 1, 8, 64, 1, 0.1, 0, None) == INV
+    assert lib.attn_bwd_dq(*([FAKE] * 8), 1, 1, 8, 128, 1, 0.1, 5, None) == INV
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.fwd(q, q, q)
