@@ -56,10 +56,18 @@ __device__ __forceinline__ constexpr int crow(int r, int g) { return 16 * (r / 8
 // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  bf16 a = (bf16)lo, b = (bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
+
+// wave-uniform copy of a value that is the same in every lane (lets the
+// compiler use scalar branches instead of exec masking)
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Eight consecutive C registers [8h, 8h+8) of a 32x32 fp32 tile, as a bf16x8
 // operand (the k = 8 * (l/32) + e slots of the next product).

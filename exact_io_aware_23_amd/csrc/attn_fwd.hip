@@ -34,11 +34,11 @@
 namespace attn {
 namespace {
 
-template <int D>
+template <int D, int QB_>
 struct FwdCfg {
   static constexpr int WAVES = 4;
-  static constexpr int QB = 2;               // 32-row query blocks per wave
-  static constexpr int BR = WAVES * QB * 32; // 256 query rows per workgroup
+  static constexpr int QB = QB_;             // 32-row query blocks per wave
+  static constexpr int BR = WAVES * QB * 32; // query rows per workgroup
   static constexpr int BC = 64;              // keys per K/V tile
   static constexpr int NCH = D / 8;          // 16-byte chunks per K row
   static constexpr int KS = D / 16;          // k-steps of S^T = K Q^T
@@ -47,15 +47,23 @@ struct FwdCfg {
   static constexpr int NKLD = BC * NCH / 256;
   static constexpr int K_ELEMS = BC * D;
   static constexpr int STAGE = 2 * BC * D;   // K and V^T
+  // one wave per SIMD when a wave owns two query blocks (more VGPRs), two otherwise
+  static constexpr int MIN_WAVES_PER_EU = QB == 1 ? 2 : 1;
 };
+
+// Lazy rescaling threshold (log2 units).  The running reference max m of a row
+// is raised only when a tile's max exceeds it by more than this, so most
+// tiles skip the O-accumulator rescale.  p = exp2(s*c - m) then stays below
+// 2^kTau; the result is unchanged (the same m is used for O and l).
+constexpr float kTau = 8.0f;
 
 __device__ __forceinline__ int vt_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
+template <int D, bool CAUSAL, int QB>
+__global__ void __launch_bounds__(256, (FwdCfg<D, QB>::MIN_WAVES_PER_EU))
 fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                 bf16* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, int total, float c) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, QB>;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
 
   const int work = xcd_remap(blockIdx.x, total);
@@ -67,13 +75,13 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   const bf16* Vh = V + head;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
   const int q0w = qt * C::BR + wave * (C::QB * 32);
 
-  // ---- tile ranges
+  // ---- tile ranges (all wave-uniform)
   const int kv_end = CAUSAL ? min(N, qt * C::BR + C::BR) : N;
   const int n_tiles = (kv_end + C::BC - 1) / C::BC;
   int wave_tiles = 0;
@@ -209,7 +217,7 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
             }
         }
       }
-      // ---- online softmax (base 2), lane-local per query row
+      // ---- online softmax (base 2), lane-local per query row, lazy rescale
       bf16x8 pop[C::QB][4];
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
@@ -218,24 +226,28 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[qb][kb][r]);
-        mx = pair_max(mx);
-        const float m_new = fmaxf(m_run[qb], mx * c);
-        const float alpha = fast_exp2(m_run[qb] - m_new);
-        m_run[qb] = m_new;
+        const float mt = pair_max(mx) * c;
+        if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + kTau) != 0) {
+          const float m_new = fmaxf(m_run[qb], mt);
+          const float alpha = fast_exp2(m_run[qb] - m_new);
+          m_run[qb] = m_new;
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[qb][dt][r] *= alpha;
+        }
+        const float mneg = -m_run[qb];
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(st[qb][kb][r], c, -m_new));
+            const float p = fast_exp2(fmaf(st[qb][kb][r], c, mneg));
             st[qb][kb][r] = p;
             rs += p;
           }
-        l_run[qb] = l_run[qb] * alpha + rs;
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[qb][dt][r] *= alpha;
+        l_run[qb] += rs;
 #pragma unroll
         for (int m = 0; m < 4; ++m) pop[qb][m] = c_to_operand(st[qb][m >> 1], m & 1);
       }
@@ -348,13 +360,15 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
   }
 }
 
+constexpr int kFwdQB = 1;  // query blocks of 32 rows per wave
+
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                              int N, float scale, hipStream_t stream) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, kFwdQB>;
   const int n_qtiles = (N + C::BR - 1) / C::BR;
   const int total = BH * n_qtiles;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, kFwdQB>), dim3(total), dim3(256), 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
                      scale * kLog2e);
   return hipGetLastError();
