@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bf16_n8192_d128_causal")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=["fwdbwd", "fwd", "copy"], default="fwdbwd",
+                    help="fwd: time the forward kernel alone (for profiling); copy: a plain 1 GiB device copy "
+                         "(calibrates the HBM byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
     return ap.parse_args()
 
@@ -93,6 +96,62 @@ def cpu_baseline(w: W.Workload, budget_s: float):
     }
 
 
+COPY_BYTES = 1 << 30
+
+
+def copy_calibration(args):
+    """A plain device-to-device copy of exactly 1 GiB (read 1 GiB, write 1 GiB).
+
+    Profiled with the FETCH_SIZE / WRITE_SIZE counters, it gives the factor
+    between what those counters report and the bytes actually moved.
+    """
+    dev = torch.device("cuda", 0)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(max(args.warmup, 1)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"metric": "device copy GB/s (counter calibration)", "value": round(2 * COPY_BYTES / dt / 1e9, 1),
+                      "unit": "GB/s", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES, "steps": args.steps}),
+          flush=True)
+    return 0
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """sha256 of the HIP source file that holds `kernel` (its code plus the shared header)."""
+    import hashlib
+
+    src = {"fwd": "attn_fwd.hip", "preprocess": "attn_bwd.hip", "dq": "attn_bwd.hip", "dkdv": "attn_bwd.hip"}[kernel]
+    h = hashlib.sha256()
+    for f in (src, "attn_common.h"):
+        with open(os.path.join(ROOT, "exact_io_aware_23_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None.
+
+    profiles/traffic_<workload>.json holds FETCH_SIZE and WRITE_SIZE per launch
+    (already scaled by the copy calibration) with the source hash they were
+    taken at; a changed kernel source makes the figure stale, so None.
+    """
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    k = rec.get("kernels", {}).get(kernel)
+    if not k or k.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    return k["hbm_bytes_per_launch"]
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -102,6 +161,8 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.which == "copy":
+        return copy_calibration(args)
     import exact_io_aware_23_amd as A
 
     A.load_library()
@@ -124,6 +185,11 @@ def main():
         A.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
         if ev is not None:
             ev[1].record(stream)
+        if args.which == "fwd":
+            if ev is not None:
+                for e in ev[2:]:
+                    e.record(stream)
+            return
         A.bwd_preprocess(o, do, delta)
         if ev is not None:
             ev[2].record(stream)
@@ -155,15 +221,17 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     F_fwd, F_bwd = w.fwd_flops(), w.bwd_flops()
+    if args.which == "fwd":
+        F_bwd = 0.0
     value = (F_fwd + F_bwd) / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = F_fwd / (per_kernel["fwd"] * 1e-3) / 1e12
     bwd_ms = per_kernel["preprocess"] + per_kernel["dq"] + per_kernel["dkdv"]
-    bwd_tflops = F_bwd / (bwd_ms * 1e-3) / 1e12
+    bwd_tflops = F_bwd / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 and F_bwd > 0 else None
 
     kf = kernel_flops(w)
-    dominant = max(names, key=lambda n: per_kernel[n])
+    dominant = "fwd" if args.which == "fwd" else max(names, key=lambda n: per_kernel[n])
     achieved = kf[dominant] / (per_kernel[dominant] * 1e-3) / 1e12
-    traffic = None
+    traffic = measured_traffic(dominant, w.name)
     roof = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
             "avg_launch_ms": round(per_kernel[dominant], 4)}
@@ -182,10 +250,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "pass": "fwd+bwd"},
+                   "pass": "fwd" if args.which == "fwd" else "fwd+bwd"},
         "fwd_tflops": round(fwd_tflops, 2),
         "fwd_frac_mfma_peak": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-        "bwd_tflops": round(bwd_tflops, 2),
+        "bwd_tflops": round(bwd_tflops, 2) if bwd_tflops else None,
         "fwdbwd_frac_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "gpu_ms_per_step": round(gpu_ms, 4),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},

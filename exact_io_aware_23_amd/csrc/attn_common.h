@@ -65,6 +65,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
+// s_waitcnt vmcnt(0) as a real instruction the compiler's wait tracking sees:
+// after it no global load is outstanding, so loads issued before a loop do not
+// make the loop body wait on loads issued inside it.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // wave-uniform copy of a value that is the same in every lane (lets the
 // compiler use scalar branches instead of exec masking)
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -86,6 +91,32 @@ __device__ __forceinline__ bf16x8 lds_read16(const bf16* base, int chunk16) {
 }
 __device__ __forceinline__ void lds_write16(bf16* base, int chunk16, const u32x4& v) {
   *reinterpret_cast<u32x4*>(base + 8 * chunk16) = v;
+}
+
+// Buffer resources: raw (stride 0) descriptors over one head's rows.  Loads
+// whose byte offset lies at or past `bytes` return zero, which gives the zero
+// fill of ragged tiles without any per-lane compare, and the per-tile offset
+// goes in a scalar register so the lane offsets stay loop-invariant.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ u32x2 bload8(rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// Buffer -> LDS direct load (buffer_load_dwordx4 ... lds): lane i of the wave
+// writes its 16 bytes at lds_wave_base + 16 * i, bypassing VGPRs.  Tracked by
+// vmcnt like any buffer load.
+__device__ __forceinline__ void bload16_lds(rsrc_t r, void* lds_wave_base, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, voff,
+                                           soff, 0, 0);
 }
 
 // 16-byte global load with zero fill when !valid

@@ -11,8 +11,9 @@
 //   used here.
 //
 // bf16 kernel design (MI355X, CDNA4):
-//   * One workgroup = 4 waves = 256 query rows; each wave owns 64 query rows as
-//     two 32-row blocks so every K or V^T fragment read from LDS feeds two MFMAs.
+//   * One workgroup = 4 waves = 128 query rows, 32 per wave; two workgroups
+//     share a CU (229 VGPRs, two waves per SIMD), so one wave's softmax runs
+//     while the other wave on the SIMD issues MFMAs.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T kept in
 //     VGPRs for the whole loop).  In the S^T layout each lane owns one query
 //     row, so the row max, the exp-sum and the O rescale stay lane-local; one
@@ -21,7 +22,11 @@
 //     bf16), V^T fragments from LDS.  V is transposed in registers while it is
 //     staged, so every LDS operand read is a conflict-free ds_read_b128.
 //   * Softmax in base 2: p = exp2(s * scale * log2(e) - m) with one FMA and one
-//     v_exp_f32 per score; L = (m + log2 l) ln 2 at the end.
+//     v_exp_f32 per score; L = (m + log2 l) ln 2 at the end.  The reference max
+//     m moves only when a tile's max exceeds it by more than 2^8 (lazy
+//     rescaling), so the O accumulators are rarely touched by the VALU.
+//   * Global loads are raw buffer loads: per-lane offsets are loop-invariant,
+//     the tile offset is a scalar, rows past N read as zero.
 //   * K/V tiles of 64 keys are double-buffered in LDS; the global loads of
 //     tile j+1 are in flight while tile j is computed.  One barrier per tile.
 //   * Causal: key tiles past a query tile's last row are never loaded; a wave
@@ -70,9 +75,10 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   const int bh = work / n_qtiles;
   const int qt = CAUSAL ? (n_qtiles - 1 - work % n_qtiles) : (work % n_qtiles);
   const size_t head = (size_t)bh * N * D;
-  const bf16* Qh = Q + head;
-  const bf16* Kh = K + head;
-  const bf16* Vh = V + head;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const rsrc_t rQ = make_rsrc(Q + head, head_bytes);
+  const rsrc_t rK = make_rsrc(K + head, head_bytes);
+  const rsrc_t rV = make_rsrc(V + head, head_bytes);
 
   const int tid = threadIdx.x;
   const int wave = uniform(tid >> 6);
@@ -94,39 +100,33 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   bf16x8 qreg[C::QB][C::KS];
 #pragma unroll
   for (int qb = 0; qb < C::QB; ++qb) {
-    const int q = q0w + 32 * qb + l32;
+    const int qoff = ((q0w + 32 * qb + l32) * D + 8 * g) * 2;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 v = gload16(Qh + (size_t)q * D + 16 * ks + 8 * g, q < N);
-      qreg[qb][ks] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int ks = 0; ks < C::KS; ++ks) qreg[qb][ks] = __builtin_bit_cast(bf16x8, bload16(rQ, qoff + 32 * ks, 0));
   }
+  wait_vmem_all();  // Q is in registers before the loop: the loop never waits on it
 
-  // ---- staging helpers
+  // ---- staging helpers: loop-invariant lane offsets, the tile offset is scalar;
+  // rows at or past N read as zero
   u32x4 kst[C::NKLD];
   uint32_t vst[8][C::DPT / 2];
   const int vkg = tid & 7;   // key group (8 keys) in the V transpose
   const int vdg = tid >> 3;  // d group (DPT columns)
+  const int koff = ((tid / C::NCH) * D + 8 * (tid % C::NCH)) * 2;  // + i * (256 / NCH) rows
+  const int voff = ((8 * vkg) * D + C::DPT * vdg) * 2;             // + e rows
 
   auto load_tile = [&](int kv0) {
+    const int soff = kv0 * D * 2;
 #pragma unroll
-    for (int i = 0; i < C::NKLD; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / C::NCH, ch = idx % C::NCH;
-      const int key = kv0 + row;
-      kst[i] = gload16(Kh + (size_t)key * D + 8 * ch, key < N);
-    }
+    for (int i = 0; i < C::NKLD; ++i) kst[i] = bload16(rK, koff + i * (256 / C::NCH) * D * 2, soff);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int key = kv0 + 8 * vkg + e;
-      const bf16* p = Vh + (size_t)key * D + C::DPT * vdg;
       if constexpr (C::DPT == 4) {
-        u32x2 z = {0u, 0u};
-        u32x2 x = key < N ? *reinterpret_cast<const u32x2*>(p) : z;
+        const u32x2 x = bload8(rV, voff + e * D * 2, soff);
         vst[e][0] = x[0];
         vst[e][1] = x[1];
       } else {
-        vst[e][0] = key < N ? *reinterpret_cast<const uint32_t*>(p) : 0u;
+        vst[e][0] = bload4(rV, voff + e * D * 2, soff);
       }
     }
   };
