@@ -19,16 +19,17 @@
 //     row, so the row max, the exp-sum and the O rescale stay lane-local; one
 //     v_permlane32_swap joins the two lane halves for the max.
 //   * O^T += V^T P^T: P^T comes straight from the S^T accumulators (rounded to
-//     bf16), V^T fragments from LDS.  V is transposed in registers while it is
-//     staged, so every LDS operand read is a conflict-free ds_read_b128.
+//     bf16); the V^T fragments come from the row-major V tile by transposing
+//     LDS reads (ds_read_b64_tr_b16), so V needs no transpose on the way in.
 //   * Softmax in base 2: p = exp2(s * scale * log2(e) - m) with one FMA and one
 //     v_exp_f32 per score; L = (m + log2 l) ln 2 at the end.  The reference max
 //     m moves only when a tile's max exceeds it by more than 2^8 (lazy
 //     rescaling), so the O accumulators are rarely touched by the VALU.
-//   * Global loads are raw buffer loads: per-lane offsets are loop-invariant,
-//     the tile offset is a scalar, rows past N read as zero.
-//   * K/V tiles of 64 keys are double-buffered in LDS; the global loads of
-//     tile j+1 are in flight while tile j is computed.  One barrier per tile.
+//   * Global loads use raw buffer resources: per-lane offsets are
+//     loop-invariant, the tile offset is a scalar, rows past N read as zero.
+//   * K/V tiles of 64 keys are double-buffered in LDS and loaded by buffer ->
+//     LDS transfers (no VGPRs, no LDS store instructions); the loads of tile
+//     j+1 are in flight while tile j is computed.  One barrier per tile.
 //   * Causal: key tiles past a query tile's last row are never loaded; a wave
 //     skips the tiles past its own last row; only diagonal (and ragged tail)
 //     tiles apply the mask.  Query tiles run longest first within a head, and
@@ -48,10 +49,9 @@ struct FwdCfg {
   static constexpr int NCH = D / 8;          // 16-byte chunks per K row
   static constexpr int KS = D / 16;          // k-steps of S^T = K Q^T
   static constexpr int DT = D / 32;          // 32-wide d tiles of O^T
-  static constexpr int DPT = D / 32;         // d columns per thread in the V transpose
   static constexpr int NKLD = BC * NCH / 256;
   static constexpr int K_ELEMS = BC * D;
-  static constexpr int STAGE = 2 * BC * D;   // K and V^T
+  static constexpr int STAGE = 2 * BC * D;   // K and V, row-major
   // one wave per SIMD when a wave owns two query blocks (more VGPRs), two otherwise
   static constexpr int MIN_WAVES_PER_EU = QB == 1 ? 2 : 1;
 };
@@ -61,8 +61,6 @@ struct FwdCfg {
 // tiles skip the O-accumulator rescale.  p = exp2(s*c - m) then stays below
 // 2^kTau; the result is unchanged (the same m is used for O and l).
 constexpr float kTau = 8.0f;
-
-__device__ __forceinline__ int vt_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 template <int D, bool CAUSAL, int QB>
 __global__ void __launch_bounds__(256, (FwdCfg<D, QB>::MIN_WAVES_PER_EU))
@@ -106,56 +104,48 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   }
   wait_vmem_all();  // Q is in registers before the loop: the loop never waits on it
 
-  // ---- staging helpers: loop-invariant lane offsets, the tile offset is scalar;
-  // rows at or past N read as zero
-  u32x4 kst[C::NKLD];
-  uint32_t vst[8][C::DPT / 2];
-  const int vkg = tid & 7;   // key group (8 keys) in the V transpose
-  const int vdg = tid >> 3;  // d group (DPT columns)
-  const int koff = ((tid / C::NCH) * D + 8 * (tid % C::NCH)) * 2;  // + i * (256 / NCH) rows
-  const int voff = ((8 * vkg) * D + C::DPT * vdg) * 2;             // + e rows
-
-  auto load_tile = [&](int kv0) {
+  // K and V tiles go straight into LDS (row-major, XOR-swizzled 16-byte chunks):
+  // wave `wave`, instruction i fills 1 KB block (wave * NKLD + i).
+  int kvoff[C::NKLD];
+#pragma unroll
+  for (int i = 0; i < C::NKLD; ++i) {
+    const int idx = (wave * C::NKLD + i) * 64 + lane;
+    const int row = idx / C::NCH, cphys = idx % C::NCH;
+    const int clog = cphys ^ (swap23(row & 15) & (C::NCH - 1));
+    kvoff[i] = (row * D + 8 * clog) * 2;
+  }
+  auto load_tile = [&](int kv0, int stage) {
     const int soff = kv0 * D * 2;
-#pragma unroll
-    for (int i = 0; i < C::NKLD; ++i) kst[i] = bload16(rK, koff + i * (256 / C::NCH) * D * 2, soff);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (C::DPT == 4) {
-        const u32x2 x = bload8(rV, voff + e * D * 2, soff);
-        vst[e][0] = x[0];
-        vst[e][1] = x[1];
-      } else {
-        vst[e][0] = bload4(rV, voff + e * D * 2, soff);
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
     bf16* Ks = smem + stage * C::STAGE;
-    bf16* Vts = Ks + C::K_ELEMS;
+    bf16* Vs = Ks + C::K_ELEMS;
 #pragma unroll
     for (int i = 0; i < C::NKLD; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / C::NCH, ch = idx % C::NCH;
-      const int swz = swap23(row & 15) & (C::NCH - 1);
-      lds_write16(Ks + row * D, ch ^ swz, kst[i]);
+      bload16_lds(rK, Ks + (wave * C::NKLD + i) * 512, kvoff[i], soff);
+      bload16_lds(rV, Vs + (wave * C::NKLD + i) * 512, kvoff[i], soff);
     }
+  };
+  // V^T operand by transposing reads: lane l = 16*G + li (li = 4 r + c1) reads
+  // key row 16 m + 8 g + r (+4 for the second half) at d column 32 dt + 16 (G & 1) + 4 c1
+  const int tr_li = lane & 15, tr_G = lane >> 4;
+  const int tr_r = tr_li >> 2, tr_c = 16 * (tr_G & 1) + 4 * (tr_li & 3);
+  auto vt_tr = [&](const bf16* Vs, int dt, int m) {
+    bf16x8 out;
 #pragma unroll
-    for (int i = 0; i < C::DPT; ++i) {
-      const int w = i >> 1;
-      u32x4 o;
+    for (int hh = 0; hh < 2; ++hh) {
+      const int row = 16 * m + 8 * g + tr_r + 4 * hh;
+      const int col = 32 * dt + tr_c;
+      const int ch = (col >> 3) ^ (swap23(row & 15) & (C::NCH - 1));
+      const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4*)(Vs + row * D + 8 * ch + (col & 7)));
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-        o[p] = (i & 1) ? pack_hi(vst[2 * p][w], vst[2 * p + 1][w]) : pack_lo(vst[2 * p][w], vst[2 * p + 1][w]);
-      const int row = C::DPT * vdg + i;
-      lds_write16(Vts + row * C::BC, vkg ^ vt_swz(row), o);
+      for (int e = 0; e < 4; ++e) out[4 * hh + e] = v[e];
     }
+    return out;
   };
 
   // per-lane LDS read offsets
   const int k_swz = (l32 & 15) & (C::NCH - 1);
   const int krow = swap23(l32);
-  const int v_swz = vt_swz(l32);
 
   f32x16 oacc[C::QB][C::DT];
 #pragma unroll
@@ -171,19 +161,19 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     l_run[qb] = 0.f;
   }
 
-  load_tile(0);
-  store_tile(0);
+  load_tile(0, 0);
+  wait_vmem_all();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int stage = j & 1;
     const int kv0 = j * C::BC;
     const bool has_next = j + 1 < n_tiles;
-    if (has_next) load_tile(kv0 + C::BC);
+    if (has_next) load_tile(kv0 + C::BC, stage ^ 1);
 
     if (j < wave_tiles) {
       const bf16* Ks = smem + stage * C::STAGE;
-      const bf16* Vts = Ks + C::K_ELEMS;
+      const bf16* Vs = Ks + C::K_ELEMS;
       // ---- S^T = K Q^T
       f32x16 st[C::QB][2];
 #pragma unroll
@@ -251,19 +241,19 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 #pragma unroll
         for (int m = 0; m < 4; ++m) pop[qb][m] = c_to_operand(st[qb][m >> 1], m & 1);
       }
-      // ---- O^T += V^T P^T
+      // ---- O^T += V^T P^T (V^T fragments by transposing LDS reads)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          const bf16x8 a = lds_read16(Vts + (32 * dt + l32) * C::BC, (2 * m + g) ^ v_swz);
+          const bf16x8 a = vt_tr(Vs, dt, m);
 #pragma unroll
           for (int qb = 0; qb < C::QB; ++qb) oacc[qb][dt] = mfma32(a, pop[qb][m], oacc[qb][dt]);
         }
       }
     }
 
-    if (has_next) store_tile(stage ^ 1);
+    wait_vmem_all();
     __syncthreads();
   }
 
