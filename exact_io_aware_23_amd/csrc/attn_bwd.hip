@@ -13,11 +13,13 @@
 //
 // Three kernels on one stream:
 //   preprocess : delta = rowsum(dO * O), fp32.
-//   dkdv       : a workgroup keeps 128 keys (32 per wave) of K and V in VGPRs
-//                and streams the 32-query blocks of Q and dO through LDS
-//                (row-major and transposed copies, both made from one global
-//                load).  Four MFMA products per block: S, dP, dV^T += dO^T P,
-//                dK^T += Q^T dS.  dK, dV accumulate in fp32 registers.
+//   dkdv       : a workgroup owns 128 keys (32 per wave): K as MFMA operands in
+//                VGPRs, V in LDS (read once from memory), and streams 32-query
+//                blocks of Q and dO into LDS by buffer -> LDS copies.  Four
+//                MFMA products per block: S, dP, dV^T += dO^T P and
+//                dK^T += Q^T dS, the dO^T and Q^T operands coming from the
+//                row-major tiles by transposing LDS reads.  dK, dV accumulate
+//                in fp32 registers; two workgroups share a CU.
 //   dq         : a workgroup keeps 128 queries (32 per wave) of Q and dO in
 //                VGPRs and streams 64-key tiles of K, V and K^T through LDS.
 //                Four products per tile: S^T = K Q^T, dP^T = V dO^T,
@@ -71,30 +73,68 @@ struct DkdvCfg {
   static constexpr int NCH = D / 8;
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
-  static constexpr int TILE = BQ * D;                      // bf16 elements of one Q or dO copy
-  static constexpr int STAGE_BYTES = 4 * TILE * 2 + 2 * BQ * 4;
+  static constexpr int QTILE = BQ * D;               // bf16 elements of one Q or dO tile
+  static constexpr int NB = QTILE * 2 / 1024 / 4;    // 1 KB transfers per wave per tile
+  static constexpr int NBV = BKV * D * 2 / 1024 / 4; // 1 KB transfers per wave for the V block
+  // LDS (bf16 elements): V block [BKV][D] | 2 stages x (Q [BQ][D], dO [BQ][D]) | 2 stages x (L', D) fp32
+  static constexpr int V_ELEMS = BKV * D;
+  static constexpr int STAGE = 2 * QTILE;
+  static constexpr int BYTES = (V_ELEMS + 2 * STAGE) * 2 + 2 * 2 * BQ * 4;
 };
 
+// XOR swizzle of the 16-byte chunks of a D-wide bf16 row (rows read 32 at a
+// time, in swap23 order or in natural order, hit distinct bank groups)
+template <int NCH>
+__device__ __forceinline__ int row_swz(int row) { return swap23(row & 15) & (NCH - 1); }
+
+// A operand of a product contracting over rows of a row-major [rows][D] LDS
+// tile (lane = d column 32 dt + l%32, k slots (l/32, e) = rows 16 h + 8 (l/32) + e),
+// by two transposing reads.  Lane l = 16 G + 4 r + c reads row 16 h + 8 g + r
+// (+4) at columns 32 dt + 16 (G & 1) + 4 c .. +3.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int dt, int h, int lane) {
+  constexpr int NCH = D / 8;
+  const int li = lane & 15, G = lane >> 4, g = lane >> 5;
+  const int col = 32 * dt + 16 * (G & 1) + 4 * (li & 3);
+  bf16x8 out;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int row = 16 * h + 8 * g + (li >> 2) + 4 * hh;
+    const int ch = (col >> 3) ^ row_swz<NCH>(row);
+    const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (__attribute__((address_space(3))) bf16x4*)(tile + row * D + 8 * ch + (col & 7)));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[4 * hh + e] = v[e];
+  }
+  return out;
+}
+
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
 bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                 const float* __restrict__ Lse, const bf16* __restrict__ dO, const float* __restrict__ Delta,
                 bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int n_ktiles, int total, float c,
                 float scale) {
   using C = DkdvCfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[C::BYTES];
+  bf16* Vs = reinterpret_cast<bf16*>(smem);
+  bf16* Xs = Vs + C::V_ELEMS;                                          // stage s: Q at s*STAGE, dO after
+  float* Fs = reinterpret_cast<float*>(smem + (C::V_ELEMS + 2 * C::STAGE) * 2);  // stage s: L' [32], delta [32]
 
   const int work = xcd_remap(blockIdx.x, total);
   const int bh = work / n_ktiles;
   const int kt = work % n_ktiles;
   const size_t head = (size_t)bh * N * D;
-  const bf16* Qh = Q + head;
-  const bf16* dOh = dO + head;
-  const float* Lh = Lse + (size_t)bh * N;
-  const float* Dh = Delta + (size_t)bh * N;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const rsrc_t rQ = make_rsrc(Q + head, head_bytes);
+  const rsrc_t rK = make_rsrc(K + head, head_bytes);
+  const rsrc_t rV = make_rsrc(V + head, head_bytes);
+  const rsrc_t rdO = make_rsrc(dO + head, head_bytes);
+  const rsrc_t rL = make_rsrc(Lse + (size_t)bh * N, (uint32_t)N * 4);
+  const rsrc_t rD = make_rsrc(Delta + (size_t)bh * N, (uint32_t)N * 4);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
@@ -102,71 +142,46 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   const int kw0 = k0 + 32 * wave;
   const int key = kw0 + l32;
 
-  // ---- K^T and V^T operands (lane = key, 8 consecutive d per k-step)
-  bf16x8 kreg[C::KS], vreg[C::KS];
+  // ---- K^T operand in VGPRs (lane = key, 8 consecutive d per k-step); V block into LDS
+  bf16x8 kreg[C::KS];
 #pragma unroll
-  for (int ks = 0; ks < C::KS; ++ks) {
-    kreg[ks] = __builtin_bit_cast(bf16x8, gload16(K + head + (size_t)key * D + 16 * ks + 8 * g, key < N));
-    vreg[ks] = __builtin_bit_cast(bf16x8, gload16(V + head + (size_t)key * D + 16 * ks + 8 * g, key < N));
-  }
-
-  // ---- staging: thread -> (which tensor, 8 queries, 4 d columns)
-  const bool st_active = tid < 2 * D;
-  const int st_which = tid / D;           // 0: Q, 1: dO
-  const int st_local = tid % D;
-  const int st_qg = st_local & 3;         // queries 8*qg .. +7
-  const int st_dc = 4 * (st_local >> 2);  // d columns st_dc .. +3
-  const bf16* st_src = st_which ? dOh : Qh;
-  u32x2 stv[8];
-  float st_f = 0.f;
-
-  auto load_tile = [&](int q0) {
-    if (st_active) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int q = q0 + 8 * st_qg + e;
-        u32x2 z = {0u, 0u};
-        stv[e] = q < N ? *reinterpret_cast<const u32x2*>(st_src + (size_t)q * D + st_dc) : z;
-      }
-    }
-    if (tid < 64) {
-      const int q = q0 + (tid & 31);
-      if (tid < 32) st_f = q < N ? Lh[q] * kLog2e : INFINITY;
-      else st_f = q < N ? Dh[q] : 0.f;
-    }
+  for (int ks = 0; ks < C::KS; ++ks)
+    kreg[ks] = __builtin_bit_cast(bf16x8, bload16(rK, (key * D + 16 * ks + 8 * g) * 2, 0));
+  // buffer -> LDS copies: 1 KB block b of a [rows][D] tile gets 16-byte chunk
+  // idx = 64 b + lane, stored at its swizzled position
+  auto tile_off = [&](int b) {
+    const int idx = b * 64 + lane;
+    const int row = idx / C::NCH, cphys = idx % C::NCH;
+    return (row * D + 8 * (cphys ^ row_swz<C::NCH>(row))) * 2;
   };
-  auto store_tile = [&](int stage) {
-    char* base = smem + stage * C::STAGE_BYTES;
-    bf16* Xs = reinterpret_cast<bf16*>(base) + st_which * C::TILE;        // row-major copy
-    bf16* XTs = reinterpret_cast<bf16*>(base) + (2 + st_which) * C::TILE; // transposed copy
-    if (st_active) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int row = 8 * st_qg + e;
-        const int swz = swap23(row & 15) & (C::NCH - 1);
-        const int chunk = st_dc >> 3;
-        *reinterpret_cast<u32x2*>(Xs + row * D + 8 * (chunk ^ swz) + (st_dc & 7)) = stv[e];
-      }
+  for (int i = 0; i < C::NBV; ++i) {
+    const int b = wave * C::NBV + i;
+    bload16_lds(rV, Vs + b * 512, tile_off(b), k0 * D * 2);
+  }
+  int qoff[C::NB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int w = i >> 1;
-        u32x4 o;
+  for (int i = 0; i < C::NB; ++i) qoff[i] = tile_off(wave * C::NB + i);
+  float stat = 0.f;  // tid < 32: L' of query q0 + tid; 32 <= tid < 64: delta
+  auto load_q = [&](int q0, int stage) {
+    bf16* Qs = Xs + stage * C::STAGE;
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
-          o[p] = (i & 1) ? pack_hi(stv[2 * p][w], stv[2 * p + 1][w]) : pack_lo(stv[2 * p][w], stv[2 * p + 1][w]);
-        const int row = st_dc + i;
-        lds_write16(XTs + row * C::BQ, st_qg ^ t_swz(row), o);
-      }
+    for (int i = 0; i < C::NB; ++i) {
+      const int b = wave * C::NB + i;
+      bload16_lds(rQ, Qs + b * 512, qoff[i], q0 * D * 2);
+      bload16_lds(rdO, Qs + C::QTILE + b * 512, qoff[i], q0 * D * 2);
     }
-    if (tid < 64) {
-      float* F = reinterpret_cast<float*>(base + 4 * C::TILE * 2);
-      F[tid] = st_f;  // Ls' at [0, 32), delta at [32, 64)
-    }
+    if (tid < 32) stat = __uint_as_float(bload4(rL, (q0 + tid) * 4, 0)) * kLog2e;
+    else if (tid < 64) stat = __uint_as_float(bload4(rD, (q0 + tid - 32) * 4, 0));
+  };
+  auto store_stat = [&](int stage) {
+    if (tid < 64) Fs[stage * 64 + tid] = stat;
   };
 
   const int a_row = swap23(l32);
   const int a_swz = (l32 & 15) & (C::NCH - 1);
-  const int tt_swz = t_swz(l32);
+  const int v_row = 32 * wave + l32;
+  const int v_swz = row_swz<C::NCH>(v_row);
 
   f32x16 dk[C::DT], dv[C::DT];
 #pragma unroll
@@ -179,44 +194,35 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 
   const int n_qt = (N + C::BQ - 1) / C::BQ;
   const int qt_begin = CAUSAL ? (k0 / C::BQ) : 0;
-
-  if (qt_begin < n_qt) {
-    load_tile(qt_begin * C::BQ);
-    store_tile(0);
-  }
+  if (qt_begin < n_qt) load_q(qt_begin * C::BQ, 0);
+  wait_vmem_all();
+  store_stat(0);
   __syncthreads();
 
   for (int it = qt_begin; it < n_qt; ++it) {
     const int stage = (it - qt_begin) & 1;
     const int q0 = it * C::BQ;
     const bool has_next = it + 1 < n_qt;
-    if (has_next) load_tile(q0 + C::BQ);
+    if (has_next) load_q(q0 + C::BQ, stage ^ 1);
 
     const bool active = kw0 < N && !(CAUSAL && q0 < kw0);
     if (active) {
-      const char* base = smem + stage * C::STAGE_BYTES;
-      const bf16* Qs = reinterpret_cast<const bf16*>(base);
-      const bf16* dOs = Qs + C::TILE;
-      const bf16* QTs = Qs + 2 * C::TILE;
-      const bf16* dOTs = Qs + 3 * C::TILE;
-      const float* Ls = reinterpret_cast<const float*>(base + 4 * C::TILE * 2);
+      const bf16* Qs = Xs + stage * C::STAGE;
+      const bf16* dOs = Qs + C::QTILE;
+      const float* Ls = Fs + stage * 64;
       const float* Ds = Ls + 32;
-
+      // ---- S = Q K^T and dP = dO V^T
       f32x16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = 0.f;
-        dp[r] = 0.f;
-      }
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
         const bf16x8 aq = lds_read16(Qs + a_row * D, (2 * ks + g) ^ a_swz);
-        s = mfma32(aq, kreg[ks], s);
+        s = mfma32(aq, kreg[ks], ks == 0 ? f32x16{} : s);
         const bf16x8 ao = lds_read16(dOs + a_row * D, (2 * ks + g) ^ a_swz);
-        dp = mfma32(ao, vreg[ks], dp);
+        const bf16x8 bv = lds_read16(Vs + v_row * D, (2 * ks + g) ^ v_swz);
+        dp = mfma32(ao, bv, ks == 0 ? f32x16{} : dp);
       }
-      // per-register query statistics: query crow(r, g) = 16*(r/8) + 8*g + r%8
-      float lrow[16], drow[16];
+      // ---- P = exp2(s c - L'), dS = P (dP - delta); query of register r: crow(r, g)
+      const bool need_mask = (kw0 + 32 > N) || (CAUSAL && q0 == kw0);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -225,44 +231,38 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
           const f32x4 dv4 = *reinterpret_cast<const f32x4*>(Ds + 16 * h + 8 * g + 4 * v4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            lrow[8 * h + 4 * v4 + i] = lv[i];
-            drow[8 * h + 4 * v4 + i] = dv4[i];
+            const int r = 8 * h + 4 * v4 + i;
+            float p = fast_exp2(fmaf(s[r], c, -lv[i]));
+            if (need_mask) {
+              const int q = q0 + crow(r, g);
+              const bool bad = (key >= N) || (CAUSAL && key > q);
+              p = bad ? 0.f : p;
+            }
+            s[r] = p;
+            dp[r] = p * (dp[r] - dv4[i]);
           }
         }
-      const bool need_mask = (kw0 + 32 > N) || (CAUSAL && q0 == kw0);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(s[r], c, -lrow[r]));
-        if (need_mask) {
-          const int q = q0 + crow(r, g);
-          const bool bad = (key >= N) || (CAUSAL && key > q);
-          p = bad ? 0.f : p;
-        }
-        s[r] = p;
-        dp[r] = p * (dp[r] - drow[r]);
-      }
-      bf16x8 pop[2], dsop[2];
+      // ---- dV^T += dO^T P and dK^T += Q^T dS (A operands by transposing reads)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        pop[h] = c_to_operand(s, h);
-        dsop[h] = c_to_operand(dp, h);
-      }
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
+        const bf16x8 pop = c_to_operand(s, h);
+        const bf16x8 dso = c_to_operand(dp, h);
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          const bf16x8 ado = lds_read16(dOTs + (32 * dt + l32) * C::BQ, (2 * h + g) ^ tt_swz);
-          dv[dt] = mfma32(ado, pop[h], dv[dt]);
-          const bf16x8 aqt = lds_read16(QTs + (32 * dt + l32) * C::BQ, (2 * h + g) ^ tt_swz);
-          dk[dt] = mfma32(aqt, dsop[h], dk[dt]);
+          dv[dt] = mfma32(tr_operand<D>(dOs, dt, h, lane), pop, dv[dt]);
+          dk[dt] = mfma32(tr_operand<D>(Qs, dt, h, lane), dso, dk[dt]);
         }
+      }
     }
 
-    if (has_next) store_tile(stage ^ 1);
+    if (has_next) {
+      wait_vmem_all();  // the next tile has landed in LDS and its statistics in `stat`
+      store_stat(stage ^ 1);
+    }
     __syncthreads();
   }
 
-  // ---- epilogue: dK = scale * dK^T^T, dV = dV^T^T
+  // ---- epilogue: dK = scale * (dK^T)^T, dV = (dV^T)^T
   if (key < N) {
     bf16* dKh = dK + head + (size_t)key * D;
     bf16* dVh = dV + head + (size_t)key * D;
