@@ -21,10 +21,11 @@
 //                row-major tiles by transposing LDS reads.  dK, dV accumulate
 //                in fp32 registers; two workgroups share a CU.
 //   dq         : a workgroup keeps 128 queries (32 per wave) of Q and dO in
-//                VGPRs and streams 64-key tiles of K, V and K^T through LDS.
-//                Four products per tile: S^T = K Q^T, dP^T = V dO^T,
-//                dQ^T += K^T dS~^T and (P K)^T += K^T P^T.  No atomics, so dQ
-//                is deterministic.
+//                VGPRs and streams 32-key tiles of K and V into LDS by buffer
+//                -> LDS copies.  Four products per tile: S^T = K Q^T,
+//                dP^T = V dO^T, dQ^T += K^T dS~^T and (P K)^T += K^T P^T, the
+//                K^T operand (shared by the last two) by transposing LDS reads.
+//                No atomics, so dQ is deterministic; two workgroups per CU.
 // Precision of delta: rowsum(dO * O) with O rounded to bf16 differs from the
 // exact sum_j P_ij dP_ij by about 2^-9 |dO| |O|, and dP - delta cancels when a
 // row's P is nearly one-hot, so that error reaches dK and dQ almost unreduced.
@@ -40,8 +41,6 @@
 namespace attn {
 namespace {
 
-__device__ __forceinline__ int t_swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }  // 64-byte rows
-__device__ __forceinline__ int vt_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }   // 128-byte rows
 
 // ------------------------------------------------------------------ preprocess
 template <int D>
@@ -286,18 +285,17 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 template <int D>
 struct DqCfg {
   static constexpr int BRQ = 128;  // queries per workgroup, 32 per wave
-  static constexpr int BC = 64;    // keys per tile
+  static constexpr int BC = 32;    // keys per tile
   static constexpr int NCH = D / 8;
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
-  static constexpr int DPT = D / 32;  // d columns per thread in the K transpose
-  static constexpr int NVLD = BC * NCH / 256;
-  static constexpr int TILE = BC * D;
-  static constexpr int STAGE = 3 * TILE;  // Ks, Vs, KTs
+  static constexpr int TILE = BC * D;                // bf16 elements of one K or V tile
+  static constexpr int NB = TILE * 2 / 1024 / 4;     // 1 KB transfers per wave per tile
+  static constexpr int STAGE = 2 * TILE;             // K then V, row-major, swizzled
 };
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
 bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
               const float* __restrict__ Lse, const bf16* __restrict__ dO, const float* __restrict__ Delta,
               bf16* __restrict__ dQ, float* __restrict__ DeltaOut, int N, int n_qtiles, int total, float c,
@@ -309,99 +307,58 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
   const int bh = work / n_qtiles;
   const int qt = CAUSAL ? (n_qtiles - 1 - work % n_qtiles) : (work % n_qtiles);
   const size_t head = (size_t)bh * N * D;
-  const bf16* Kh = K + head;
-  const bf16* Vh = V + head;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const rsrc_t rQ = make_rsrc(Q + head, head_bytes);
+  const rsrc_t rK = make_rsrc(K + head, head_bytes);
+  const rsrc_t rV = make_rsrc(V + head, head_bytes);
+  const rsrc_t rdO = make_rsrc(dO + head, head_bytes);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
   const int q0w = qt * C::BRQ + 32 * wave;
   const int q = q0w + l32;
 
+  // ---- Q^T and dO^T operands in VGPRs (lane = query, 8 consecutive d per k-step)
   bf16x8 qreg[C::KS], doreg[C::KS];
+  const int qoff = (q * D + 8 * g) * 2;
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
-    qreg[ks] = __builtin_bit_cast(bf16x8, gload16(Q + head + (size_t)q * D + 16 * ks + 8 * g, q < N));
-    doreg[ks] = __builtin_bit_cast(bf16x8, gload16(dO + head + (size_t)q * D + 16 * ks + 8 * g, q < N));
+    qreg[ks] = __builtin_bit_cast(bf16x8, bload16(rQ, qoff + 32 * ks, 0));
+    doreg[ks] = __builtin_bit_cast(bf16x8, bload16(rdO, qoff + 32 * ks, 0));
   }
   const float lq = q < N ? Lse[(size_t)bh * N + q] * kLog2e : INFINITY;
   const float dq_delta = q < N ? Delta[(size_t)bh * N + q] : 0.f;  // approximate delta (from bf16 O)
   float d_exact = 0.f;  // this lane's share of sum_j P_qj dP_qj
+  wait_vmem_all();
 
   const int kv_end = CAUSAL ? min(N, qt * C::BRQ + C::BRQ) : N;
   const int n_tiles = (kv_end + C::BC - 1) / C::BC;
   int wave_tiles = 0;
   if (q0w < N) wave_tiles = CAUSAL ? (min(N, q0w + 32) + C::BC - 1) / C::BC : n_tiles;
 
-  // staging: V row-major with 16-byte loads; K with the transposing mapping
-  u32x4 vst[C::NVLD];
-  uint32_t kst[8][C::DPT / 2];
-  const int kkg = tid & 7;
-  const int kdg = tid >> 3;
-  auto load_tile = [&](int kv0) {
+  // buffer -> LDS copies of the K and V tiles (1 KB block b gets chunk 64 b + lane)
+  int toff[C::NB];
 #pragma unroll
-    for (int i = 0; i < C::NVLD; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / C::NCH, ch = idx % C::NCH;
-      const int key = kv0 + row;
-      vst[i] = gload16(Vh + (size_t)key * D + 8 * ch, key < N);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = kv0 + 8 * kkg + e;
-      const bf16* p = Kh + (size_t)key * D + C::DPT * kdg;
-      if constexpr (C::DPT == 4) {
-        u32x2 z = {0u, 0u};
-        u32x2 x = key < N ? *reinterpret_cast<const u32x2*>(p) : z;
-        kst[e][0] = x[0];
-        kst[e][1] = x[1];
-      } else {
-        kst[e][0] = key < N ? *reinterpret_cast<const uint32_t*>(p) : 0u;
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
+  for (int i = 0; i < C::NB; ++i) {
+    const int idx = (wave * C::NB + i) * 64 + lane;
+    const int row = idx / C::NCH, cphys = idx % C::NCH;
+    toff[i] = (row * D + 8 * (cphys ^ row_swz<C::NCH>(row))) * 2;
+  }
+  auto load_tile = [&](int kv0, int stage) {
     bf16* Ks = smem + stage * C::STAGE;
-    bf16* Vs = Ks + C::TILE;
-    bf16* KTs = Ks + 2 * C::TILE;
 #pragma unroll
-    for (int i = 0; i < C::NVLD; ++i) {
-      const int idx = tid + 256 * i;
-      const int row = idx / C::NCH, ch = idx % C::NCH;
-      lds_write16(Vs + row * D, ch ^ (swap23(row & 15) & (C::NCH - 1)), vst[i]);
-    }
-    const int dcol0 = C::DPT * kdg;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int row = 8 * kkg + e;
-      const int swz = swap23(row & 15) & (C::NCH - 1);
-      bf16* dst = Ks + row * D + 8 * ((dcol0 >> 3) ^ swz) + (dcol0 & 7);
-      if constexpr (C::DPT == 4) {
-        u32x2 x;
-        x[0] = kst[e][0];
-        x[1] = kst[e][1];
-        *reinterpret_cast<u32x2*>(dst) = x;
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = kst[e][0];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::DPT; ++i) {
-      const int w = i >> 1;
-      u32x4 o;
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        o[p] = (i & 1) ? pack_hi(kst[2 * p][w], kst[2 * p + 1][w]) : pack_lo(kst[2 * p][w], kst[2 * p + 1][w]);
-      const int row = dcol0 + i;
-      lds_write16(KTs + row * C::BC, kkg ^ vt_swz(row), o);
+    for (int i = 0; i < C::NB; ++i) {
+      const int b = wave * C::NB + i;
+      bload16_lds(rK, Ks + b * 512, toff[i], kv0 * D * 2);
+      bload16_lds(rV, Ks + C::TILE + b * 512, toff[i], kv0 * D * 2);
     }
   };
 
   const int a_row = swap23(l32);
   const int a_swz = (l32 & 15) & (C::NCH - 1);
-  const int v_swz = vt_swz(l32);
 
   f32x16 dq[C::DT], pk[C::DT];  // dQ^T with the approximate delta, and (P K)^T
 #pragma unroll
@@ -412,66 +369,56 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
       pk[dt][r] = 0.f;
     }
 
-  load_tile(0);
-  store_tile(0);
+  load_tile(0, 0);
+  wait_vmem_all();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
     const int stage = j & 1;
     const int kv0 = j * C::BC;
-    const bool has_next = j + 1 < n_tiles;
-    if (has_next) load_tile(kv0 + C::BC);
+    if (j + 1 < n_tiles) load_tile(kv0 + C::BC, stage ^ 1);
 
     if (j < wave_tiles) {
       const bf16* Ks = smem + stage * C::STAGE;
       const bf16* Vs = Ks + C::TILE;
-      const bf16* KTs = Ks + 2 * C::TILE;
-      f32x16 st[2], dpt[2];
+      // ---- S^T = K Q^T and dP^T = V dO^T (K, V rows read in swap23 order)
+      f32x16 st, dpt;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          st[kb][r] = 0.f;
-          dpt[kb][r] = 0.f;
-        }
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 ak = lds_read16(Ks + (32 * kb + a_row) * D, (2 * ks + g) ^ a_swz);
-          st[kb] = mfma32(ak, qreg[ks], st[kb]);
-          const bf16x8 av = lds_read16(Vs + (32 * kb + a_row) * D, (2 * ks + g) ^ a_swz);
-          dpt[kb] = mfma32(av, doreg[ks], dpt[kb]);
-        }
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8 ak = lds_read16(Ks + a_row * D, (2 * ks + g) ^ a_swz);
+        st = mfma32(ak, qreg[ks], ks == 0 ? f32x16{} : st);
+        const bf16x8 av = lds_read16(Vs + a_row * D, (2 * ks + g) ^ a_swz);
+        dpt = mfma32(av, doreg[ks], ks == 0 ? f32x16{} : dpt);
+      }
+      // ---- P, the exact-delta partial sums and dS~ = P (dP - delta~); key of register r: crow(r, g)
       const bool need_mask = (kv0 + C::BC > N) || (CAUSAL && kv0 + C::BC - 1 > q0w);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(fmaf(st[kb][r], c, -lq));
-          if (need_mask) {
-            const int key = kv0 + 32 * kb + crow(r, g);
-            const bool bad = (key >= N) || (CAUSAL && key > q);
-            p = bad ? 0.f : p;
-          }
-          d_exact = fmaf(p, dpt[kb][r], d_exact);
-          dpt[kb][r] = p * (dpt[kb][r] - dq_delta);
-          st[kb][r] = p;
+      for (int r = 0; r < 16; ++r) {
+        float p = fast_exp2(fmaf(st[r], c, -lq));
+        if (need_mask) {
+          const int key = kv0 + crow(r, g);
+          const bool bad = (key >= N) || (CAUSAL && key > q);
+          p = bad ? 0.f : p;
         }
+        d_exact = fmaf(p, dpt[r], d_exact);
+        dpt[r] = p * (dpt[r] - dq_delta);
+        st[r] = p;
+      }
+      // ---- dQ^T += K^T dS~^T and (P K)^T += K^T P^T, K^T by transposing reads
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const bf16x8 dso = c_to_operand(dpt[m >> 1], m & 1);
-        const bf16x8 po = c_to_operand(st[m >> 1], m & 1);
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 dso = c_to_operand(dpt, h);
+        const bf16x8 po = c_to_operand(st, h);
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          const bf16x8 akt = lds_read16(KTs + (32 * dt + l32) * C::BC, (2 * m + g) ^ v_swz);
+          const bf16x8 akt = tr_operand<D>(Ks, dt, h, lane);
           dq[dt] = mfma32(akt, dso, dq[dt]);
           pk[dt] = mfma32(akt, po, pk[dt]);
         }
       }
     }
 
-    if (has_next) store_tile(stage ^ 1);
+    wait_vmem_all();  // the next tile has landed in LDS
     __syncthreads();
   }
 
