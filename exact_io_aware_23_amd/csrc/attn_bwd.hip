@@ -81,27 +81,34 @@ struct DkdvCfg {
   static constexpr int BYTES = (V_ELEMS + 2 * STAGE) * 2 + 2 * 2 * BQ * 4;
 };
 
-// XOR swizzle of the 16-byte chunks of a D-wide bf16 row (rows read 32 at a
-// time, in swap23 order or in natural order, hit distinct bank groups)
-template <int NCH>
-__device__ __forceinline__ int row_swz(int row) { return swap23(row & 15) & (NCH - 1); }
-
 // A operand of a product contracting over rows of a row-major [rows][D] LDS
 // tile (lane = d column 32 dt + l%32, k slots (l/32, e) = rows 16 h + 8 (l/32) + e),
 // by two transposing reads.  Lane l = 16 G + 4 r + c reads row 16 h + 8 g + r
-// (+4) at columns 32 dt + 16 (G & 1) + 4 c .. +3.
+// (+4 for the second read) at columns 32 dt + 16 (G & 1) + 4 c .. +3.
+// With chunk_swz the element offset of that read is
+//   (base[hh] ^ (32 dt)) + 16 h D,
+// base[hh] = (8 g + r + 4 hh) D + 32 r' + 8 ((2 (G & 1) + c / 2) ^ (2 g + hh)) + 4 (c & 1),
+// r' = r (D = 128) or (r / 2) & 1 (D = 64): the column group term occupies bits
+// the row offset leaves zero, so one v_xor per read addresses any dt.
 template <int D>
-__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int dt, int h, int lane) {
-  constexpr int NCH = D / 8;
-  const int li = lane & 15, G = lane >> 4, g = lane >> 5;
-  const int col = 32 * dt + 16 * (G & 1) + 4 * (li & 3);
+struct TrBase {
+  int b[2];
+  __device__ __forceinline__ explicit TrBase(int lane) {
+    const int li = lane & 15, G = lane >> 4, g = lane >> 5;
+    const int r = li >> 2, c = li & 3;
+    const int rr = D == 128 ? r : ((r >> 1) & 1);
+    const int x = 2 * (G & 1) + (c >> 1);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) b[hh] = (8 * g + r + 4 * hh) * D + 32 * rr + 8 * (x ^ (2 * g + hh)) + 4 * (c & 1);
+  }
+};
+template <int D>
+__device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int dt, int h, const TrBase<D>& tb) {
   bf16x8 out;
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh) {
-    const int row = 16 * h + 8 * g + (li >> 2) + 4 * hh;
-    const int ch = (col >> 3) ^ row_swz<NCH>(row);
     const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (__attribute__((address_space(3))) bf16x4*)(tile + row * D + 8 * ch + (col & 7)));
+        (__attribute__((address_space(3))) bf16x4*)(tile + ((tb.b[hh] ^ (32 * dt)) + 16 * h * D)));
 #pragma unroll
     for (int e = 0; e < 4; ++e) out[4 * hh + e] = v[e];
   }
@@ -151,7 +158,7 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   auto tile_off = [&](int b) {
     const int idx = b * 64 + lane;
     const int row = idx / C::NCH, cphys = idx % C::NCH;
-    return (row * D + 8 * (cphys ^ row_swz<C::NCH>(row))) * 2;
+    return (row * D + 8 * (cphys ^ chunk_swz<C::NCH>(row))) * 2;
   };
 #pragma unroll
   for (int i = 0; i < C::NBV; ++i) {
@@ -178,9 +185,10 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   };
 
   const int a_row = swap23(l32);
-  const int a_swz = (l32 & 15) & (C::NCH - 1);
+  const int a_swz = chunk_swz<C::NCH>(a_row);
+  const TrBase<D> trb(lane);
   const int v_row = 32 * wave + l32;
-  const int v_swz = row_swz<C::NCH>(v_row);
+  const int v_swz = chunk_swz<C::NCH>(v_row);
 
   f32x16 dk[C::DT], dv[C::DT];
 #pragma unroll
@@ -248,8 +256,8 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         const bf16x8 dso = c_to_operand(dp, h);
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          dv[dt] = mfma32(tr_operand<D>(dOs, dt, h, lane), pop, dv[dt]);
-          dk[dt] = mfma32(tr_operand<D>(Qs, dt, h, lane), dso, dk[dt]);
+          dv[dt] = mfma32(tr_operand<D>(dOs, dt, h, trb), pop, dv[dt]);
+          dk[dt] = mfma32(tr_operand<D>(Qs, dt, h, trb), dso, dk[dt]);
         }
       }
     }
@@ -345,7 +353,7 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
   for (int i = 0; i < C::NB; ++i) {
     const int idx = (wave * C::NB + i) * 64 + lane;
     const int row = idx / C::NCH, cphys = idx % C::NCH;
-    toff[i] = (row * D + 8 * (cphys ^ row_swz<C::NCH>(row))) * 2;
+    toff[i] = (row * D + 8 * (cphys ^ chunk_swz<C::NCH>(row))) * 2;
   }
   auto load_tile = [&](int kv0, int stage) {
     bf16* Ks = smem + stage * C::STAGE;
@@ -358,7 +366,8 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
   };
 
   const int a_row = swap23(l32);
-  const int a_swz = (l32 & 15) & (C::NCH - 1);
+  const int a_swz = chunk_swz<C::NCH>(a_row);
+  const TrBase<D> trb(lane);
 
   f32x16 dq[C::DT], pk[C::DT];  // dQ^T with the approximate delta, and (P K)^T
 #pragma unroll
@@ -411,7 +420,7 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
         const bf16x8 po = c_to_operand(st, h);
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          const bf16x8 akt = tr_operand<D>(Ks, dt, h, lane);
+          const bf16x8 akt = tr_operand<D>(Ks, dt, h, trb);
           dq[dt] = mfma32(akt, dso, dq[dt]);
           pk[dt] = mfma32(akt, po, pk[dt]);
         }

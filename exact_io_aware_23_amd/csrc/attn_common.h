@@ -48,6 +48,24 @@ __device__ __forceinline__ int swap23(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
+// XOR swizzle of the 16-byte chunks of a row-major LDS tile with NCH chunks
+// per row.  Physical chunk = logical chunk ^ chunk_swz(row).  It serves both
+// read patterns used on the tiles:
+//   * ds_read_b128 of one chunk from 16 consecutive rows (any order of the
+//     low 4 row bits): the swizzle is a bijection of those bits, so the 16
+//     lanes hit 16 different 16-byte bank groups;
+//   * ds_read_b64_tr_b16 of 4 adjacent chunks from rows {r, r+8} x r = 0..3
+//     (+4): the 4 rows r land in 4 different groups of 4 chunks (2-way at
+//     most, the minimum for the 512 bytes such a read moves).
+// D = 128 (16 chunks, 256-byte rows): swap the two 2-bit fields of row & 15.
+// D = 64 (8 chunks, two rows per 256-byte bank window): bit 2 = row bit 1,
+// bits 0-1 = row bits 2-3.
+template <int NCH>
+__device__ __forceinline__ int chunk_swz(int row) {
+  if constexpr (NCH == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
 // Row index (within a 32-row tile whose A-operand rows were read in swap23
 // order) held by C register r in lane half g:
 //   swap23(8*(r/4) + 4*g + r%4) = 16*(r/8) + 8*g + r%8

@@ -111,7 +111,7 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   for (int i = 0; i < C::NKLD; ++i) {
     const int idx = (wave * C::NKLD + i) * 64 + lane;
     const int row = idx / C::NCH, cphys = idx % C::NCH;
-    const int clog = cphys ^ (swap23(row & 15) & (C::NCH - 1));
+    const int clog = cphys ^ (chunk_swz<C::NCH>(row));
     kvoff[i] = (row * D + 8 * clog) * 2;
   }
   auto load_tile = [&](int kv0, int stage) {
@@ -124,19 +124,25 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
       bload16_lds(rV, Vs + (wave * C::NKLD + i) * 512, kvoff[i], soff);
     }
   };
-  // V^T operand by transposing reads: lane l = 16*G + li (li = 4 r + c1) reads
-  // key row 16 m + 8 g + r (+4 for the second half) at d column 32 dt + 16 (G & 1) + 4 c1
-  const int tr_li = lane & 15, tr_G = lane >> 4;
-  const int tr_r = tr_li >> 2, tr_c = 16 * (tr_G & 1) + 4 * (tr_li & 3);
+  // V^T operand by transposing reads: lane l = 16 G + 4 r + c reads key row
+  // 16 m + 8 g + r (+4 for the second half) at d columns 32 dt + 16 (G & 1) + 4 c;
+  // with chunk_swz the element offset is (vbase[hh] ^ (32 dt)) + 16 m D
+  int vbase[2];
+  {
+    const int li = lane & 15, G = lane >> 4;
+    const int r = li >> 2, cc = li & 3;
+    const int rr = D == 128 ? r : ((r >> 1) & 1);
+    const int x = 2 * (G & 1) + (cc >> 1);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      vbase[hh] = (8 * g + r + 4 * hh) * D + 32 * rr + 8 * (x ^ (2 * g + hh)) + 4 * (cc & 1);
+  }
   auto vt_tr = [&](const bf16* Vs, int dt, int m) {
     bf16x8 out;
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int row = 16 * m + 8 * g + tr_r + 4 * hh;
-      const int col = 32 * dt + tr_c;
-      const int ch = (col >> 3) ^ (swap23(row & 15) & (C::NCH - 1));
       const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-          (__attribute__((address_space(3))) bf16x4*)(Vs + row * D + 8 * ch + (col & 7)));
+          (__attribute__((address_space(3))) bf16x4*)(Vs + ((vbase[hh] ^ (32 * dt)) + 16 * m * D)));
 #pragma unroll
       for (int e = 0; e < 4; ++e) out[4 * hh + e] = v[e];
     }
@@ -144,8 +150,8 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   };
 
   // per-lane LDS read offsets
-  const int k_swz = (l32 & 15) & (C::NCH - 1);
   const int krow = swap23(l32);
+  const int k_swz = chunk_swz<C::NCH>(krow);
 
   f32x16 oacc[C::QB][C::DT];
 #pragma unroll
