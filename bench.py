@@ -56,8 +56,8 @@ def kernel_flops(w: W.Workload):
     A forward contraction over the allowed (query, key) pairs costs
     2*B*H*N^2*d (halved when causal); the forward has two, the backward five
     (the recomputed Q K^T, dO V^T, P^T dO, dS^T Q and dS K).  dkdv executes four
-    of the five; dq executes dS K (its recomputed Q K^T, dO V^T and the P K
-    correction are not counted); preprocess is memory traffic only.
+    of the five; dq executes dS K (its recomputed Q K^T and dO V^T are not
+    counted); preprocess is memory traffic only.
     """
     one = w.fwd_flops() / 2
     return {"fwd": 2 * one, "dkdv": 4 * one, "dq": 1 * one, "preprocess": 0.0}

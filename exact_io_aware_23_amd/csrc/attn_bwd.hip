@@ -22,18 +22,19 @@
 //                in fp32 registers; two workgroups share a CU.
 //   dq         : a workgroup keeps 128 queries (32 per wave) of Q and dO in
 //                VGPRs and streams 32-key tiles of K and V into LDS by buffer
-//                -> LDS copies.  Four products per tile: S^T = K Q^T,
-//                dP^T = V dO^T, dQ^T += K^T dS~^T and (P K)^T += K^T P^T, the
-//                K^T operand (shared by the last two) by transposing LDS reads.
-//                No atomics, so dQ is deterministic; two workgroups per CU.
-// Precision of delta: rowsum(dO * O) with O rounded to bf16 differs from the
+//                -> LDS copies.  Three products per tile: S^T = K Q^T,
+//                dP^T = V dO^T and dQ^T += K^T dS^T, the K^T operand by
+//                transposing LDS reads.  No atomics, so dQ is deterministic;
+//                two workgroups per CU.  On the way it sums delta exactly.
+// Precision of delta: rowsum(dO * O) with O as stored (bf16) differs from the
 // exact sum_j P_ij dP_ij by about 2^-9 |dO| |O|, and dP - delta cancels when a
-// row's P is nearly one-hot, so that error reaches dK and dQ almost unreduced.
-// The dq kernel therefore runs first: it forms dS~ = P (dP - delta~) with the
-// approximate delta~ (small after the cancellation, so its bf16 rounding is
-// harmless), accumulates the exact delta = sum_j P_ij dP_ij in fp32 on the way,
-// and adds the correction (delta~ - delta) (P K) at the end.  dkdv then uses
-// the exact delta.  Order: preprocess -> dq -> dkdv.
+// row's P is nearly one-hot, so that error passes into dS almost unreduced.
+// In dQ = scale dS K it is multiplied by K and stays well inside the bf16
+// tolerance, so the dq kernel uses delta~ = rowsum(dO * O) as the backward
+// defines it.  In dK = scale dS^T Q it is multiplied by Q, and a query row of
+// large norm carries it into dK at full size; so the dq kernel also sums
+// delta = sum_j P_ij dP_ij in fp32 from the same P and dP it forms, and dkdv
+// runs after it with that exact delta.  Order: preprocess -> dq -> dkdv.
 // Both recompute P with p = exp2(s * scale * log2 e - L * log2 e).
 #include "attn_common.h"
 #include "attn_launch.h"
@@ -229,7 +230,16 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         dp = mfma32(ao, bv, ks == 0 ? f32x16{} : dp);
       }
       // ---- P = exp2(s c - L'), dS = P (dP - delta); query of register r: crow(r, g)
+      // masked scores become -inf, so exp2 gives exactly 0 (one branch per tile)
       const bool need_mask = (kw0 + 32 > N) || (CAUSAL && q0 == kw0);
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = q0 + crow(r, g);
+          const bool bad = (key >= N) || (CAUSAL && key > q);
+          s[r] = bad ? -INFINITY : s[r];
+        }
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -239,12 +249,7 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 8 * h + 4 * v4 + i;
-            float p = fast_exp2(fmaf(s[r], c, -lv[i]));
-            if (need_mask) {
-              const int q = q0 + crow(r, g);
-              const bool bad = (key >= N) || (CAUSAL && key > q);
-              p = bad ? 0.f : p;
-            }
+            const float p = fast_exp2(fmaf(s[r], c, -lv[i]));
             s[r] = p;
             dp[r] = p * (dp[r] - dv4[i]);
           }
@@ -338,7 +343,7 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
     doreg[ks] = __builtin_bit_cast(bf16x8, bload16(rdO, qoff + 32 * ks, 0));
   }
   const float lq = q < N ? Lse[(size_t)bh * N + q] * kLog2e : INFINITY;
-  const float dq_delta = q < N ? Delta[(size_t)bh * N + q] : 0.f;  // approximate delta (from bf16 O)
+  const float dq_delta = q < N ? Delta[(size_t)bh * N + q] : 0.f;  // rowsum(dO * O), O as stored
   float d_exact = 0.f;  // this lane's share of sum_j P_qj dP_qj
   wait_vmem_all();
 
@@ -369,13 +374,12 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
   const int a_swz = chunk_swz<C::NCH>(a_row);
   const TrBase<D> trb(lane);
 
-  f32x16 dq[C::DT], pk[C::DT];  // dQ^T with the approximate delta, and (P K)^T
+  f32x16 dq[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       dq[dt][r] = 0.f;
-      pk[dt][r] = 0.f;
     }
 
   load_tile(0, 0);
@@ -399,30 +403,32 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
         const bf16x8 av = lds_read16(Vs + a_row * D, (2 * ks + g) ^ a_swz);
         dpt = mfma32(av, doreg[ks], ks == 0 ? f32x16{} : dpt);
       }
-      // ---- P, the exact-delta partial sums and dS~ = P (dP - delta~); key of register r: crow(r, g)
+      // ---- P, the exact-delta partial sums and dS = P (dP - delta~); key of register r: crow(r, g)
+      // masked scores become -inf, so exp2 gives exactly 0 (one branch per tile)
       const bool need_mask = (kv0 + C::BC > N) || (CAUSAL && kv0 + C::BC - 1 > q0w);
+      if (need_mask) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(st[r], c, -lq));
-        if (need_mask) {
+        for (int r = 0; r < 16; ++r) {
           const int key = kv0 + crow(r, g);
           const bool bad = (key >= N) || (CAUSAL && key > q);
-          p = bad ? 0.f : p;
+          st[r] = bad ? -INFINITY : st[r];
         }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(st[r], c, -lq));
         d_exact = fmaf(p, dpt[r], d_exact);
         dpt[r] = p * (dpt[r] - dq_delta);
         st[r] = p;
       }
-      // ---- dQ^T += K^T dS~^T and (P K)^T += K^T P^T, K^T by transposing reads
+      // ---- dQ^T += K^T dS^T, K^T by transposing reads
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const bf16x8 dso = c_to_operand(dpt, h);
-        const bf16x8 po = c_to_operand(st, h);
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
           const bf16x8 akt = tr_operand<D>(Ks, dt, h, trb);
           dq[dt] = mfma32(akt, dso, dq[dt]);
-          pk[dt] = mfma32(akt, po, pk[dt]);
         }
       }
     }
@@ -431,10 +437,8 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
     __syncthreads();
   }
 
-  // exact delta_q = sum_j P_qj dP_qj; dS was formed with the approximate delta,
-  // so dQ = scale * (dS~ K + (delta~ - delta) P K)
+  // exact delta_q = sum_j P_qj dP_qj, handed to the dK/dV kernel
   d_exact = pair_sum(d_exact);
-  const float corr = dq_delta - d_exact;
   if (q < N) {
     bf16* dQh = dQ + head + (size_t)q * D;
 #pragma unroll
@@ -444,7 +448,7 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
         const int dcol = 32 * dt + 8 * a + 4 * g;
         float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = scale * fmaf(corr, pk[dt][4 * a + i], dq[dt][4 * a + i]);
+        for (int i = 0; i < 4; ++i) v[i] = scale * dq[dt][4 * a + i];
         u32x2 w;
         w[0] = pack_bf16x2(v[0], v[1]);
         w[1] = pack_bf16x2(v[2], v[3]);

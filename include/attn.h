@@ -87,7 +87,8 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
 
 /* Backward stage 1: delta~_i = sum_k dO_ik * O_ik in fp32.  Mathematically
  * equal to sum_j P_ij dP_ij (the row term of the softmax Jacobian); with O
- * rounded to bf16 it is an approximation that stage 2 refines.
+ * rounded to bf16 it is an approximation: stage 2 uses it for dQ and sums the
+ * exact value for stage 3.
  *   o, dout : inputs [B,H,N,d] of `dtype`; delta : output [B,H,N] fp32. */
 attn_status_t attn_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int H,
                                   int N, int d, attn_dtype_t dtype, void* stream);
@@ -106,11 +107,11 @@ attn_status_t attn_bwd_dkdv(const void* q, const void* k, const void* v, const f
 
 /* Backward stage 2: dQ and the exact delta.  One workgroup per block of
  * queries keeps Q and dO on chip and visits the key blocks, recomputing
- * P = exp(S - L) and dP = dO V^T per block.  It forms dS~ = P (dP - delta~)
- * with the approximate delta~ from stage 1, accumulates
- * delta_i = sum_j P_ij dP_ij in fp32 as it goes, and returns
- * dQ = scale (dS~ K + (delta~ - delta) P K), which equals scale dS K with the
- * exact delta.  No atomics: the result is deterministic.
+ * P = exp(S - L) and dP = dO V^T per block.  It returns
+ * dQ = scale P (dP - delta~) K with delta~ from stage 1 (the rowsum of
+ * dO * O as stored), and sums delta_i = sum_j P_ij dP_ij in fp32 from the same
+ * P and dP for stage 3, whose dK multiplies delta's error by Q.  No atomics:
+ * the result is deterministic.
  *   q, k, v, dout : inputs of `dtype`; lse, delta : fp32 inputs [B,H,N]
  *   dq            : output [B,H,N,d] of `dtype`
  *   delta_out     : output [B,H,N] fp32, the exact delta (may not alias delta). */
