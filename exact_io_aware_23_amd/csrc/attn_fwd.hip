@@ -12,8 +12,11 @@
 //
 // bf16 kernel design (MI355X, CDNA4):
 //   * One workgroup = 4 waves = 128 query rows, 32 per wave; two workgroups
-//     share a CU (229 VGPRs, two waves per SIMD), so one wave's softmax runs
-//     while the other wave on the SIMD issues MFMAs.
+//     share a CU (224 VGPRs, two waves per SIMD).
+//   * Software pipeline inside each wave: the scores of tile j+1 are formed
+//     while tile j's exponentials run, then tile j's P V, all in one basic
+//     block whose instruction order is pinned (sched_group_barrier), so the
+//     VALU work sits in the shadow of the MFMAs of the same wave.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T kept in
 //     VGPRs for the whole loop).  In the S^T layout each lane owns one query
 //     row, so the row max, the exp-sum and the O rescale stay lane-local; one
@@ -28,8 +31,9 @@
 //   * Global loads use raw buffer resources: per-lane offsets are
 //     loop-invariant, the tile offset is a scalar, rows past N read as zero.
 //   * K/V tiles of 64 keys are double-buffered in LDS and loaded by buffer ->
-//     LDS transfers (no VGPRs, no LDS store instructions); the loads of tile
-//     j+1 are in flight while tile j is computed.  One barrier per tile.
+//     LDS transfers (no VGPRs, no LDS store instructions): while a wave works
+//     on K(j+1) and V(j), K(j+2) and V(j+1) are in flight.  One barrier per
+//     tile.
 //   * Causal: key tiles past a query tile's last row are never loaded; a wave
 //     skips the tiles past its own last row; only diagonal (and ragged tail)
 //     tiles apply the mask.  Query tiles run longest first within a head, and
@@ -40,20 +44,17 @@
 namespace attn {
 namespace {
 
-template <int D, int QB_>
+template <int D>
 struct FwdCfg {
   static constexpr int WAVES = 4;
-  static constexpr int QB = QB_;             // 32-row query blocks per wave
-  static constexpr int BR = WAVES * QB * 32; // query rows per workgroup
+  static constexpr int BR = WAVES * 32;      // query rows per workgroup, 32 per wave
   static constexpr int BC = 64;              // keys per K/V tile
   static constexpr int NCH = D / 8;          // 16-byte chunks per K row
   static constexpr int KS = D / 16;          // k-steps of S^T = K Q^T
   static constexpr int DT = D / 32;          // 32-wide d tiles of O^T
   static constexpr int NKLD = BC * NCH / 256;
   static constexpr int K_ELEMS = BC * D;
-  static constexpr int STAGE = 2 * BC * D;   // K and V, row-major
-  // one wave per SIMD when a wave owns two query blocks (more VGPRs), two otherwise
-  static constexpr int MIN_WAVES_PER_EU = QB == 1 ? 2 : 1;
+  static constexpr int STAGE = 2 * BC * D;   // one slot: a K tile then a V tile, row-major
 };
 
 // Lazy rescaling threshold (log2 units).  The running reference max m of a row
@@ -62,11 +63,11 @@ struct FwdCfg {
 // 2^kTau; the result is unchanged (the same m is used for O and l).
 constexpr float kTau = 8.0f;
 
-template <int D, bool CAUSAL, int QB>
-__global__ void __launch_bounds__(256, (FwdCfg<D, QB>::MIN_WAVES_PER_EU))
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 2)
 fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                 bf16* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, int total, float c) {
-  using C = FwdCfg<D, QB>;
+  using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
 
   const int work = xcd_remap(blockIdx.x, total);
@@ -83,47 +84,49 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int g = lane >> 5;
-  const int q0w = qt * C::BR + wave * (C::QB * 32);
+  const int q0w = qt * C::BR + wave * 32;
+  const int q = q0w + l32;
 
-  // ---- tile ranges (all wave-uniform)
+  // ---- tile ranges (all wave-uniform): the workgroup loads n_tiles tiles,
+  // this wave computes the first wave_tiles of them
   const int kv_end = CAUSAL ? min(N, qt * C::BR + C::BR) : N;
   const int n_tiles = (kv_end + C::BC - 1) / C::BC;
   int wave_tiles = 0;
-  if (q0w < N) {
-    const int wend = CAUSAL ? min(N, q0w + C::QB * 32) : N;
-    wave_tiles = (wend + C::BC - 1) / C::BC;
-  }
+  if (q0w < N) wave_tiles = ((CAUSAL ? min(N, q0w + 32) : N) + C::BC - 1) / C::BC;
+  // tile j needs the mask when it holds keys past N or (causal) past this wave's first row
+  auto needs_mask = [&](int j) { return (j + 1) * C::BC > N || (CAUSAL && (j + 1) * C::BC - 1 > q0w); };
 
   // ---- Q^T operand in registers: lane (l32, g) holds Q[q][16ks + 8g .. +7]
-  bf16x8 qreg[C::QB][C::KS];
+  bf16x8 qreg[C::KS];
+  {
+    const int qoff = (q * D + 8 * g) * 2;
 #pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    const int qoff = ((q0w + 32 * qb + l32) * D + 8 * g) * 2;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) qreg[qb][ks] = __builtin_bit_cast(bf16x8, bload16(rQ, qoff + 32 * ks, 0));
+    for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, bload16(rQ, qoff + 32 * ks, 0));
   }
-  wait_vmem_all();  // Q is in registers before the loop: the loop never waits on it
 
   // K and V tiles go straight into LDS (row-major, XOR-swizzled 16-byte chunks):
-  // wave `wave`, instruction i fills 1 KB block (wave * NKLD + i).
+  // wave `wave`, instruction i fills 1 KB block (wave * NKLD + i) of the tile.
   int kvoff[C::NKLD];
 #pragma unroll
   for (int i = 0; i < C::NKLD; ++i) {
     const int idx = (wave * C::NKLD + i) * 64 + lane;
     const int row = idx / C::NCH, cphys = idx % C::NCH;
-    const int clog = cphys ^ (chunk_swz<C::NCH>(row));
-    kvoff[i] = (row * D + 8 * clog) * 2;
+    kvoff[i] = (row * D + 8 * (cphys ^ chunk_swz<C::NCH>(row))) * 2;
   }
-  auto load_tile = [&](int kv0, int stage) {
-    const int soff = kv0 * D * 2;
-    bf16* Ks = smem + stage * C::STAGE;
-    bf16* Vs = Ks + C::K_ELEMS;
+  auto load_k = [&](int j, int slot) {
+    bf16* Ks = smem + slot * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < C::NKLD; ++i) {
-      bload16_lds(rK, Ks + (wave * C::NKLD + i) * 512, kvoff[i], soff);
-      bload16_lds(rV, Vs + (wave * C::NKLD + i) * 512, kvoff[i], soff);
-    }
+    for (int i = 0; i < C::NKLD; ++i) bload16_lds(rK, Ks + (wave * C::NKLD + i) * 512, kvoff[i], j * C::BC * D * 2);
   };
+  auto load_v = [&](int j, int slot) {
+    bf16* Vs = smem + slot * C::STAGE + C::K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < C::NKLD; ++i) bload16_lds(rV, Vs + (wave * C::NKLD + i) * 512, kvoff[i], j * C::BC * D * 2);
+  };
+
+  // S^T operand reads: K row swap23(l32) of each 32-key half
+  const int krow = swap23(l32);
+  const int k_swz = chunk_swz<C::NCH>(krow);
   // V^T operand by transposing reads: lane l = 16 G + 4 r + c reads key row
   // 16 m + 8 g + r (+4 for the second half) at d columns 32 dt + 16 (G & 1) + 4 c;
   // with chunk_swz the element offset is (vbase[hh] ^ (32 dt)) + 16 m D
@@ -149,141 +152,173 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     return out;
   };
 
-  // per-lane LDS read offsets
-  const int krow = swap23(l32);
-  const int k_swz = chunk_swz<C::NCH>(krow);
+  f32x16 oacc[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m_run = -1e30f, l_run = 0.f;
 
-  f32x16 oacc[C::QB][C::DT];
+  // ---- the pieces of one tile
+  // S^T = K Q^T for the K tile in `slot`
+  auto scores = [&](int slot, f32x16 (&st)[2]) {
+    const bf16* Ks = smem + slot * C::STAGE;
 #pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb)
+    for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[qb][dt][r] = 0.f;
-  float m_run[C::QB], l_run[C::QB];
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    m_run[qb] = -1e30f;
-    l_run[qb] = 0.f;
-  }
-
-  load_tile(0, 0);
-  wait_vmem_all();
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int stage = j & 1;
-    const int kv0 = j * C::BC;
-    const bool has_next = j + 1 < n_tiles;
-    if (has_next) load_tile(kv0 + C::BC, stage ^ 1);
-
-    if (j < wave_tiles) {
-      const bf16* Ks = smem + stage * C::STAGE;
-      const bf16* Vs = Ks + C::K_ELEMS;
-      // ---- S^T = K Q^T
-      f32x16 st[C::QB][2];
-#pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) st[qb][kb][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const bf16x8 a = lds_read16(Ks + (32 * kb + krow) * D, (2 * ks + g) ^ k_swz);
-#pragma unroll
-          for (int qb = 0; qb < C::QB; ++qb) st[qb][kb] = mfma32(a, qreg[qb][ks], st[qb][kb]);
-        }
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = lds_read16(Ks + (32 * kb + krow) * D, (2 * ks + g) ^ k_swz);
+        st[kb] = mfma32(a, qreg[ks], ks == 0 ? f32x16{} : st[kb]);
       }
-      // ---- mask (diagonal / ragged tiles only)
-      const bool need_mask = (kv0 + C::BC > N) || (CAUSAL && kv0 + C::BC - 1 > q0w);
-      if (need_mask) {
+  };
+  // masked scores become -inf (keys past N, and causal keys past the row)
+  auto mask = [&](f32x16 (&st)[2], int j) {
 #pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb) {
-          const int q = q0w + 32 * qb + l32;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kv0 + 32 * kb + crow(r, g);
-              const bool bad = (key >= N) || (CAUSAL && key > q);
-              st[qb][kb][r] = bad ? -INFINITY : st[qb][kb][r];
-            }
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = j * C::BC + 32 * kb + crow(r, g);
+        const bool bad = (key >= N) || (CAUSAL && key > q);
+        st[kb][r] = bad ? -INFINITY : st[kb][r];
       }
-      // ---- online softmax (base 2), lane-local per query row, lazy rescale
-      bf16x8 pop[C::QB][4];
+  };
+  // this row's tile max in log2 units
+  auto tile_max = [&](const f32x16 (&st)[2]) {
+    float mx = -INFINITY;
 #pragma unroll
-      for (int qb = 0; qb < C::QB; ++qb) {
-        float mx = -INFINITY;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[qb][kb][r]);
-        const float mt = pair_max(mx) * c;
-        if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + kTau) != 0) {
-          const float m_new = fmaxf(m_run[qb], mt);
-          const float alpha = fast_exp2(m_run[qb] - m_new);
-          m_run[qb] = m_new;
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[qb][dt][r] *= alpha;
-        }
-        const float mneg = -m_run[qb];
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = fast_exp2(fmaf(st[qb][kb][r], c, mneg));
-            st[qb][kb][r] = p;
-            rs += p;
-          }
-        l_run[qb] += rs;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) pop[qb][m] = c_to_operand(st[qb][m >> 1], m & 1);
-      }
-      // ---- O^T += V^T P^T (V^T fragments by transposing LDS reads)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) {
-          const bf16x8 a = vt_tr(Vs, dt, m);
-#pragma unroll
-          for (int qb = 0; qb < C::QB; ++qb) oacc[qb][dt] = mfma32(a, pop[qb][m], oacc[qb][dt]);
-        }
-      }
-    }
-
-    wait_vmem_all();
-    __syncthreads();
-  }
-
-  // ---- epilogue: O = O_acc / l, L = (m + log2 l) ln 2
-  bf16* Oh = O + head;
-  float* Lh = L + (size_t)bh * N;
-#pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    const int q = q0w + 32 * qb + l32;
-    const float lt = pair_sum(l_run[qb]);
-    if (q < N) {
-      const float inv = 1.0f / lt;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
+    return pair_max(mx) * c;
+  };
+  // raise the reference max when the tile's max passed it by more than kTau
+  auto rescale = [&](float mt) {
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int dcol = 32 * dt + 8 * a + 4 * g;
-          u32x2 w;
-          w[0] = pack_bf16x2(oacc[qb][dt][4 * a + 0] * inv, oacc[qb][dt][4 * a + 1] * inv);
-          w[1] = pack_bf16x2(oacc[qb][dt][4 * a + 2] * inv, oacc[qb][dt][4 * a + 3] * inv);
-          *reinterpret_cast<u32x2*>(Oh + (size_t)q * D + dcol) = w;
-        }
-      if (g == 0) Lh[q] = (m_run[qb] + log2f(lt)) * kLn2;
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
     }
+  };
+  // p = exp2(s c - m) in place, the row sum into l, and the P^T operands
+  auto exps = [&](f32x16 (&st)[2], bf16x8 (&pop)[4]) {
+    const float mneg = -m_run;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(st[kb][r], c, mneg));
+        st[kb][r] = p;
+        rs += p;
+      }
+    l_run += rs;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) pop[m] = c_to_operand(st[m >> 1], m & 1);
+  };
+  // O^T += V^T P^T for the V tile in `slot`
+  auto pv = [&](int slot, const bf16x8 (&pop)[4]) {
+    const bf16* Vs = smem + slot * C::STAGE + C::K_ELEMS;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = mfma32(vt_tr(Vs, dt, m), pop[m], oacc[dt]);
+  };
+
+  // Instruction order inside the two straight-line phases of a pipelined step.
+  // Phase A, the scores of tile j+1 with tile j's exponentials: each score
+  // MFMA takes one K read issued four ahead and a share of the VALU work.
+  // Phase B, tile j's P V with tile j+1's max: each P V MFMA takes two
+  // transposing reads and a little VALU.
+  constexpr int SM = 2 * C::KS, PVM = 4 * C::DT;  // MFMAs per phase
+  auto pin_a = [&]() {
+    constexpr int VA = (120 + SM - 1) / SM;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < SM - 4) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, VA, 0);
+    }
+  };
+  auto pin_b = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < PVM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < PVM - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 3, 0);
+    }
+  };
+
+  // ---- software pipeline.  Slot s of LDS holds K and V tiles of the same
+  // parity.  Iteration j reads K(j+1) (scores of the next tile) and V(j) (this
+  // tile's P V), and loads K(j+2) over K(j) and V(j+1) over V(j-1), both read
+  // before the previous barrier.  The scores of tile j+1 are independent of
+  // tile j's exponentials, and tile j's P V of tile j+1's max, so each pair
+  // sits in one basic block for the scheduler to interleave.
+  load_k(0, 0);
+  load_v(0, 0);
+  if (n_tiles > 1) load_k(1, 1);
+  wait_vmem_all();
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  if (wave_tiles > 0) {
+    scores(0, sa);
+    if (needs_mask(0)) mask(sa, 0);
+    rescale(tile_max(sa));
+  }
+  __syncthreads();  // every wave has read K(0) before K(2) is loaded over it
+
+  // `par` = j & 1, passed as a literal so every LDS address is a constant
+  // offset from one per-lane base
+  auto step = [&](int j, int par, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    if (j + 2 < n_tiles) load_k(j + 2, par);
+    if (j + 1 < n_tiles) load_v(j + 1, par ^ 1);
+    if (j < wave_tiles) {
+      // The scores of tile j+1 are formed even when this wave has no such
+      // tile: the slot then holds another K tile (in bounds), every one of
+      // its keys lies past this wave's rows or past N, so the mask sets them
+      // all to -inf, and the rescale is skipped.  One code path per step.
+      bf16x8 pop[4];
+      scores(par ^ 1, nxt);
+      exps(cur, pop);
+      pv(par, pop);
+      pin_a();
+      pin_b();
+      if (needs_mask(j + 1)) mask(nxt, j + 1);
+      if (j + 1 < wave_tiles) rescale(tile_max(nxt));
+    }
+    wait_vmem_all();  // K(j+2) and V(j+1) have landed in LDS
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < n_tiles; j += 2) {
+    step(j, 0, sa, sb);
+    step(j + 1, 1, sb, sa);
+  }
+  if (j < n_tiles) step(j, 0, sa, sb);
+
+  // ---- epilogue: O = O_acc / l, L = (m + log2 l) ln 2
+  const float lt = pair_sum(l_run);
+  if (q < N) {
+    bf16* Oh = O + head + (size_t)q * D;
+    const float inv = 1.0f / lt;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int dcol = 32 * dt + 8 * a + 4 * g;
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[dt][4 * a + 0] * inv, oacc[dt][4 * a + 1] * inv);
+        w[1] = pack_bf16x2(oacc[dt][4 * a + 2] * inv, oacc[dt][4 * a + 3] * inv);
+        *reinterpret_cast<u32x2*>(Oh + dcol) = w;
+      }
+    if (g == 0) L[(size_t)bh * N + q] = (m_run + log2f(lt)) * kLn2;
   }
 }
 
@@ -356,15 +391,13 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
   }
 }
 
-constexpr int kFwdQB = 1;  // query blocks of 32 rows per wave
-
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                              int N, float scale, hipStream_t stream) {
-  using C = FwdCfg<D, kFwdQB>;
+  using C = FwdCfg<D>;
   const int n_qtiles = (N + C::BR - 1) / C::BR;
   const int total = BH * n_qtiles;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, kFwdQB>), dim3(total), dim3(256), 0, stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, stream,
                      (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
                      scale * kLog2e);
   return hipGetLastError();
