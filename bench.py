@@ -3,9 +3,11 @@
 One step = attn_fwd followed by the backward stages (preprocess, dq, dkdv) on
 one batch of the headline workload, B=2, H=32, N=8192, d=128, bf16, causal,
 with inputs already resident in device memory.  Prints one JSON line.
+Workloads without a backward pass (fp32_small, bf16_n256_d64_short) time the
+forward alone.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--batch B] [--heads H] [--no-cpu-baseline]
 
 Reported:
   value         whole-step attention TFLOP/s, (F_fwd + F_bwd) / t_step, with the
@@ -14,7 +16,10 @@ Reported:
   fwd_tflops    forward alone, from HIP events around attn_fwd
   roofline      the kernel with the largest share of the step, against the
                 bf16 dense MFMA peak; its average launch time comes from HIP
-                events recorded around it inside the timed steps
+                events recorded around it inside the timed steps.  A forward
+                whose FLOP/byte ratio is below the machine balance (MFMA peak /
+                HBM peak) is priced against HBM bandwidth instead, and the fp32
+                forward against the fp32 vector peak
   cpu_baseline  the fp64 CPU oracle, timed on a bounded sample of heads
 """
 from __future__ import annotations
@@ -33,6 +38,7 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak (published)
 HBM_PEAK_GBS = 8000.0
 
 
@@ -42,6 +48,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bf16_n8192_d128_causal")
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's B")
+    ap.add_argument("--heads", type=int, default=None, help="override the workload's H (e.g. one GPU's share of heads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=["fwdbwd", "fwd", "copy"], default="fwdbwd",
                     help="fwd: time the forward kernel alone (for profiling); copy: a plain 1 GiB device copy "
@@ -166,9 +174,13 @@ def main():
     import exact_io_aware_23_amd as A
 
     A.load_library()
+    import dataclasses
+
     w = W.BY_NAME[args.workload]
+    w = dataclasses.replace(w, B=args.batch or w.B, H=args.heads or w.H)
+    fwd_only = args.which == "fwd" or not w.backward
     dev = torch.device("cuda", 0)
-    inp = W.draw_workload(w)
+    inp = W.draw_workload(w, B=w.B, H=w.H)
     q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
     B, H, N, d = q.shape
     o = torch.empty_like(q)
@@ -185,7 +197,7 @@ def main():
         A.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
         if ev is not None:
             ev[1].record(stream)
-        if args.which == "fwd":
+        if fwd_only:
             if ev is not None:
                 for e in ev[2:]:
                     e.record(stream)
@@ -221,7 +233,7 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     F_fwd, F_bwd = w.fwd_flops(), w.bwd_flops()
-    if args.which == "fwd":
+    if fwd_only:
         F_bwd = 0.0
     value = (F_fwd + F_bwd) / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = F_fwd / (per_kernel["fwd"] * 1e-3) / 1e12
@@ -229,11 +241,18 @@ def main():
     bwd_tflops = F_bwd / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 and F_bwd > 0 else None
 
     kf = kernel_flops(w)
-    dominant = "fwd" if args.which == "fwd" else max(names, key=lambda n: per_kernel[n])
-    achieved = kf[dominant] / (per_kernel[dominant] * 1e-3) / 1e12
-    traffic = measured_traffic(dominant, w.name)
-    roof = {"kernel": dominant, "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+    dominant = "fwd" if fwd_only else max(names, key=lambda n: per_kernel[n])
+    t_dom = per_kernel[dominant] * 1e-3
+    balance = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # FLOP per byte
+    if w.dtype == "f32":
+        bound, achieved, peak, unit = "alu", kf["fwd"] / t_dom / 1e12, FP32_VECTOR_PEAK_TFLOPS, "TFLOP/s"
+    elif dominant == "fwd" and w.fwd_flops() / w.fwd_bytes() < balance:
+        bound, achieved, peak, unit = "hbm", w.fwd_bytes() / t_dom / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", kf[dominant] / t_dom / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
+    traffic = measured_traffic(dominant, w.name) if (w.B, w.H) == (W.BY_NAME[w.name].B, W.BY_NAME[w.name].H) else None
+    roof = {"kernel": dominant, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
             "avg_launch_ms": round(per_kernel[dominant], 4)}
 
     out = {
@@ -247,10 +266,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "pass": "fwd" if args.which == "fwd" else "fwd+bwd"},
+                   "pass": "fwd" if fwd_only else "fwd+bwd"},
         "fwd_tflops": round(fwd_tflops, 2),
         "fwd_frac_mfma_peak": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "bwd_tflops": round(bwd_tflops, 2) if bwd_tflops else None,
