@@ -29,7 +29,12 @@ Readings where the pages are silent (each listed in the design notes):
     log of the scaled, masked scores;
   * the backward is the exact gradient of O with respect to Q, K and V for an
     upstream gradient dO; its formulas come from differentiating the
-    definition (the pages only say the gradients are the same).
+    definition (the pages only say the gradients are the same);
+  * block-sparse attention ([talk], questions after the method part: the
+    tiled method also takes imposed sparsity, skipping the computation it
+    removes) keeps the pairs whose 128 x 128 block is switched on in a block
+    mask, on top of the causal mask; a query row with no allowed key has
+    P = 0, O = 0 and L = -inf, and contributes no gradient.
 """
 from __future__ import annotations
 
@@ -39,6 +44,7 @@ from typing import Iterable, Sequence
 import numpy as np
 
 NEG_INF = -np.inf
+BLOCK = 128  # side of one block of a block-sparse mask
 
 
 def _f64(x) -> np.ndarray:
@@ -51,58 +57,79 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def scores_head(q: np.ndarray, k: np.ndarray, scale: float, causal: bool) -> np.ndarray:
-    """S = scale * Q K^T for one head, with -inf above the diagonal when causal.
+def allowed_pairs(n_q: int, n_k: int, causal: bool, block_mask=None) -> np.ndarray:
+    """Boolean [n_q, n_k]: True where query i may attend key j.
+
+    Causal: j <= i.  Block-sparse: the (i // BLOCK, j // BLOCK) entry of the
+    block mask is nonzero ([talk], questions after the method part).
+    """
+    i = np.arange(n_q)[:, None]
+    j = np.arange(n_k)[None, :]
+    ok = np.ones((n_q, n_k), dtype=bool)
+    if causal:
+        ok &= j <= i
+    if block_mask is not None:
+        bm = np.asarray(block_mask) != 0
+        ok &= bm[i // BLOCK, j // BLOCK]
+    return ok
+
+
+def scores_head(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, block_mask=None) -> np.ndarray:
+    """S = scale * Q K^T for one head, with -inf wherever a pair is not allowed.
 
     [video] 01:04: scores are Q times K transposed over sqrt(D); [slides] block
     scores formula.  [talk] background: the mask sets entries to -inf before
     the softmax.
     """
     s = scale * (q @ k.T)
-    if causal:
-        n_q, n_k = s.shape
-        i = np.arange(n_q)[:, None]
-        j = np.arange(n_k)[None, :]
-        s = np.where(j > i, NEG_INF, s)
+    if causal or block_mask is not None:
+        s = np.where(allowed_pairs(s.shape[0], s.shape[1], causal, block_mask), s, NEG_INF)
     return s
 
 
 def _safe_softmax(s: np.ndarray):
     """Row softmax with the row max subtracted first ([slides] safe-softmax formula).
 
-    Returns P, the row max m and the row sum l of exp(s - m).
+    Returns P, the row max m and the row sum l of exp(s - m).  A row with no
+    finite score (every key masked) has m = -inf, l = 0 and P = 0.
     """
     m = s.max(axis=1)
-    e = np.exp(s - m[:, None])  # exp(-inf) = 0 at masked entries
+    live = np.isfinite(m)
+    e = np.exp(s - np.where(live, m, 0.0)[:, None])  # exp(-inf) = 0 at masked entries
     l = e.sum(axis=1)
-    return e / l[:, None], m, l
+    p = np.where(live[:, None], e / np.where(live, l, 1.0)[:, None], 0.0)
+    return p, m, l
 
 
-def forward_head(q, k, v, scale: float, causal: bool):
+def forward_head(q, k, v, scale: float, causal: bool, block_mask=None):
     """Standard attention for one head: S, P = softmax(S), O = P V, and L = m + ln l.
 
     [video] 01:04 for S, P, O; 06:52-07:24 for the per-row statistics kept for
-    the backward, stored here as the single logsumexp L.
-    Returns (O [N,d], L [N], P [N,N]).
+    the backward, stored here as the single logsumexp L.  `block_mask`
+    ([ceil(N/128), ceil(N/128)], nonzero = on) restricts the allowed pairs.
+    Returns (O [N,d], L [N], P [N,N]); a row with no allowed key has O = 0
+    and L = -inf.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
-    s = scores_head(q, k, scale, causal)
+    s = scores_head(q, k, scale, causal, block_mask)
     p, m, l = _safe_softmax(s)
     o = p @ v
-    lse = m + np.log(l)
+    with np.errstate(divide="ignore"):
+        lse = np.where(np.isfinite(m), m + np.log(l), NEG_INF)
     return o, lse, p
 
 
-def backward_head(q, k, v, do, scale: float, causal: bool):
+def backward_head(q, k, v, do, scale: float, causal: bool, block_mask=None):
     """Exact gradients of O = softmax(scale Q K^T + mask) V for one head.
 
     With P from the definition: dV = P^T dO; dP = dO V^T; the softmax Jacobian
     gives dS = P * (dP - rowsum(P * dP)); then dQ = scale dS K and
-    dK = scale dS^T Q.  Masked entries have P = 0, hence dS = 0.
+    dK = scale dS^T Q.  Masked entries have P = 0, hence dS = 0; a row with
+    no allowed key contributes nothing.
     Returns (dQ, dK, dV, Delta) where Delta_i = sum_j P_ij dP_ij.
     """
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
-    _, _, p = forward_head(q, k, v, scale, causal)
+    _, _, p = forward_head(q, k, v, scale, causal, block_mask)
     dv = p.T @ do
     dp = do @ v.T
     delta = (p * dp).sum(axis=1)
@@ -112,9 +139,18 @@ def backward_head(q, k, v, do, scale: float, causal: bool):
     return dq, dk, dv, delta
 
 
-def attention_forward(q, k, v, scale: float, causal: bool):
+def head_block_mask(block_mask, b: int, h: int, H: int):
+    """The [nb, nb] block mask of head (b, h) from a [1 or B*H, nb, nb] array (or None)."""
+    if block_mask is None:
+        return None
+    bm = np.asarray(block_mask)
+    return bm[0] if bm.shape[0] == 1 else bm[b * H + h]
+
+
+def attention_forward(q, k, v, scale: float, causal: bool, block_mask=None):
     """Forward over all (batch, head) pairs of [B, H, N, d] inputs.
 
+    `block_mask`: None, or [1 or B*H, ceil(N/128), ceil(N/128)] (nonzero = on).
     Returns O [B, H, N, d] and L [B, H, N] in float64.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -123,11 +159,12 @@ def attention_forward(q, k, v, scale: float, causal: bool):
     lse = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):
-            o[b, h], lse[b, h], _ = forward_head(q[b, h], k[b, h], v[b, h], scale, causal)
+            o[b, h], lse[b, h], _ = forward_head(q[b, h], k[b, h], v[b, h], scale, causal,
+                                                 head_block_mask(block_mask, b, h, H))
     return o, lse
 
 
-def attention_backward(q, k, v, do, scale: float, causal: bool):
+def attention_backward(q, k, v, do, scale: float, causal: bool, block_mask=None):
     """Backward over all (batch, head) pairs; returns dQ, dK, dV in float64."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     B, H, N, d = q.shape
@@ -136,25 +173,39 @@ def attention_backward(q, k, v, do, scale: float, causal: bool):
     dv = np.empty_like(v)
     for b in range(B):
         for h in range(H):
-            dq[b, h], dk[b, h], dv[b, h], _ = backward_head(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
+            dq[b, h], dk[b, h], dv[b, h], _ = backward_head(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal,
+                                                            head_block_mask(block_mask, b, h, H))
     return dq, dk, dv
 
 
-def forward_rows(q_rows, rows: Sequence[int], k, v, scale: float, causal: bool):
+def _row_scores(q_row, i: int, k, scale: float, causal: bool, block_mask):
+    """Scores of query row i against all keys, -inf where the pair is not allowed."""
+    s = scale * (k @ q_row)
+    if causal:
+        s[i + 1:] = NEG_INF
+    if block_mask is not None:
+        on = np.asarray(block_mask)[i // BLOCK] != 0
+        s = np.where(np.repeat(on, BLOCK)[: s.shape[0]], s, NEG_INF)
+    return s
+
+
+def forward_rows(q_rows, rows: Sequence[int], k, v, scale: float, causal: bool, block_mask=None):
     """O and L for selected query rows of one head, each computed on its own.
 
     Row i needs only q_i and all of K and V: s = scale * K q_i (masked to
-    j <= i when causal), then the safe softmax and the weighted sum of V.
-    Costs O(N d) per row, so it serves sampled checks at long N.
+    j <= i when causal, and to the row's blocks under a block mask), then the
+    safe softmax and the weighted sum of V.  Costs O(N d) per row, so it
+    serves sampled checks at long N.  A row with no allowed key: O = 0, L = -inf.
     """
     q_rows, k, v = _f64(q_rows), _f64(k), _f64(v)
     o = np.empty((len(rows), v.shape[1]))
     lse = np.empty(len(rows))
     for r, i in enumerate(rows):
-        s = scale * (k @ q_rows[r])
-        if causal:
-            s[i + 1:] = NEG_INF
+        s = _row_scores(q_rows[r], i, k, scale, causal, block_mask)
         m = s.max()
+        if m == NEG_INF:
+            o[r], lse[r] = 0.0, NEG_INF
+            continue
         e = np.exp(s - m)
         l = e.sum()
         o[r] = (e / l) @ v
@@ -162,19 +213,20 @@ def forward_rows(q_rows, rows: Sequence[int], k, v, scale: float, causal: bool):
     return o, lse
 
 
-def dq_rows(q_rows, do_rows, rows: Sequence[int], k, v, scale: float, causal: bool):
+def dq_rows(q_rows, do_rows, rows: Sequence[int], k, v, scale: float, causal: bool, block_mask=None):
     """dQ for selected query rows of one head, each computed on its own.
 
     Row i: P_i from the row's softmax, dP_ij = dO_i . V_j,
     Delta_i = sum_j P_ij dP_ij (= dO_i . O_i), dS_ij = P_ij (dP_ij - Delta_i),
-    dQ_i = scale * sum_j dS_ij K_j.
+    dQ_i = scale * sum_j dS_ij K_j.  A row with no allowed key: dQ_i = 0.
     """
     q_rows, do_rows, k, v = _f64(q_rows), _f64(do_rows), _f64(k), _f64(v)
     out = np.empty((len(rows), k.shape[1]))
     for r, i in enumerate(rows):
-        s = scale * (k @ q_rows[r])
-        if causal:
-            s[i + 1:] = NEG_INF
+        s = _row_scores(q_rows[r], i, k, scale, causal, block_mask)
+        if s.max() == NEG_INF:
+            out[r] = 0.0
+            continue
         e = np.exp(s - s.max())
         p = e / e.sum()
         dp = v @ do_rows[r]
