@@ -8,6 +8,11 @@ forward alone.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
                     [--batch B] [--heads H] [--no-cpu-baseline]
+                    [--block-density P]
+
+--block-density P times the block-sparse entry points instead, on a seeded
+random mask over 128 x 128 blocks (each block on with probability P, diagonal
+blocks always on), counting only the allowed (query, key) pairs.
 
 Reported:
   value         whole-step attention TFLOP/s, (F_fwd + F_bwd) / t_step, with the
@@ -55,6 +60,8 @@ def parse():
                     help="fwd: time the forward kernel alone (for profiling); copy: a plain 1 GiB device copy "
                          "(calibrates the HBM byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
+    ap.add_argument("--block-density", type=float, default=None,
+                    help="time attn_fwd_block_sparse + attn_bwd_block_sparse on a random block mask of this density")
     return ap.parse_args()
 
 
@@ -160,6 +167,93 @@ def measured_traffic(kernel: str, workload: str):
     return k["hbm_bytes_per_launch"]
 
 
+def allowed_pairs_per_head(mask: torch.Tensor, N: int, causal: bool) -> torch.Tensor:
+    """Allowed (query, key) pairs of each head under a [heads, nb, nb] block mask (and the causal mask)."""
+    nb = mask.shape[-1]
+    start = torch.arange(nb, dtype=torch.int64) * 128
+    size = torch.clamp(N - start, max=128)  # rows (or keys) in each block
+    pairs = size[:, None] * size[None, :]
+    if causal:
+        # keys j <= i: blocks left of the diagonal count fully, the diagonal one triangularly
+        r, c = torch.meshgrid(torch.arange(nb), torch.arange(nb), indexing="ij")
+        tri = size * (size + 1) // 2
+        pairs = torch.where(c < r, pairs, torch.where(c == r, torch.diag(tri), torch.zeros_like(pairs)))
+    return (mask.to(torch.int64).cpu() * pairs).sum(dim=(1, 2))
+
+
+def bench_block_sparse(args, w):
+    """Forward + backward of block-sparse attention; prints one JSON line."""
+    import exact_io_aware_23_amd as A
+
+    dev = torch.device("cuda", 0)
+    inp = W.draw_workload(w, B=w.B, H=w.H)
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    B, H, N, d = q.shape
+    nb = (N + 127) // 128
+    g = torch.Generator().manual_seed(1234)
+    mask = (torch.rand((B * H, nb, nb), generator=g) < args.block_density).to(torch.uint8)
+    mask[:, torch.arange(nb), torch.arange(nb)] = 1
+    pairs = int(allowed_pairs_per_head(mask, N, w.causal).sum())
+    F_fwd = 4.0 * d * pairs
+    F_bwd = 2.5 * F_fwd
+    m = mask.to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(A.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        A.fwd_block_sparse(q, k, v, m, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        A.bwd_block_sparse(q, k, v, o, lse, do, m, scale=w.scale, causal=w.causal, workspace=ws, dq=dq, dk=dk,
+                           dv=dv)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    t_fwd = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    t_bwd = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    achieved = F_fwd / (t_fwd * 1e-3) / 1e12
+    density = pairs / (B * H * (N * (N + 1) / 2 if w.causal else N * N))
+    out = {
+        "metric": "block-sparse attention TFLOP/s fwd and fwd+bwd (allowed pairs only)",
+        "value": round((F_fwd + F_bwd) / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "pass": "fwd+bwd",
+                   "block_density": args.block_density, "allowed_fraction": round(density, 4),
+                   "mask": "random 128x128 blocks, torch seed 1234, diagonal blocks on"},
+        "fwd_tflops": round(achieved, 2),
+        "bwd_tflops": round(F_bwd / (t_bwd * 1e-3) / 1e12, 2),
+        "kernel_ms": {"fwd": round(t_fwd, 4), "bwd (preprocess+dq+dkdv)": round(t_bwd, 4)},
+        "roofline": {"kernel": "fwd", "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(t_fwd, 4)},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -178,6 +272,8 @@ def main():
 
     w = W.BY_NAME[args.workload]
     w = dataclasses.replace(w, B=args.batch or w.B, H=args.heads or w.H)
+    if args.block_density is not None:
+        return bench_block_sparse(args, w)
     fwd_only = args.which == "fwd" or not w.backward
     dev = torch.device("cuda", 0)
     inp = W.draw_workload(w, B=w.B, H=w.H)

@@ -10,11 +10,13 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     abi_version,
     bwd,
+    bwd_block_sparse,
     bwd_dkdv,
     bwd_dq,
     bwd_preprocess,
     bwd_workspace_bytes,
     fwd,
+    fwd_block_sparse,
     load_library,
     status_string,
 )

@@ -29,6 +29,9 @@ _SIGNATURES = {
     "attn_bwd_preprocess": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_fwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _S, _I, _I, _I, _I, _I, _F,
+                                   _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_abi_version": (_I, []),
 }
@@ -143,6 +146,58 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, w
     _call("attn_bwd", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, N, d,
           _dtype_code(q), _default_scale(d, scale), int(bool(causal)), _stream(q.device))
+    return dq, dk, dv
+
+
+def _block_mask(block_mask: torch.Tensor, B: int, H: int, N: int) -> torch.Tensor:
+    """Check a block mask: uint8 on the GPU, [nb, nb] or [1 or B*H, nb, nb], nb = ceil(N/128)."""
+    nb = (N + 127) // 128
+    if not isinstance(block_mask, torch.Tensor):
+        raise TypeError("block_mask must be a torch.Tensor")
+    m = block_mask[None] if block_mask.dim() == 2 else block_mask
+    if m.dim() != 3 or m.shape[1:] != (nb, nb) or m.shape[0] not in (1, B * H):
+        raise ValueError(f"block_mask has shape {tuple(block_mask.shape)}, expected ({nb}, {nb}) or "
+                         f"(1 or {B * H}, {nb}, {nb})")
+    _check("block_mask", m, tuple(m.shape), torch.uint8)
+    return m
+
+
+def fwd_block_sparse(q, k, v, block_mask, scale: float | None = None, causal: bool = False, out=None, lse=None):
+    """attn_fwd_block_sparse; returns (O, L).  A row with no allowed key gets O = 0, L = -inf."""
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    m = _block_mask(block_mask, B, H, N)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check("out", out, (B, H, N, d), q.dtype)
+    _check("lse", lse, (B, H, N), torch.float32)
+    _call("attn_fwd_block_sparse", q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+          m.data_ptr(), m.shape[0], B, H, N, d, _dtype_code(q), _default_scale(d, scale), int(bool(causal)),
+          _stream(q.device))
+    return out, lse
+
+
+def bwd_block_sparse(q, k, v, o, lse, do, block_mask, scale: float | None = None, causal: bool = False,
+                     workspace=None, dq=None, dk=None, dv=None):
+    """attn_bwd_block_sparse; returns (dQ, dK, dV)."""
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    _check("lse", lse, (B, H, N), torch.float32)
+    m = _block_mask(block_mask, B, H, N)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    ws_bytes = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _call("attn_bwd_block_sparse", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+          do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), m.data_ptr(), m.shape[0],
+          workspace.data_ptr(), workspace.numel(), B, H, N, d, _dtype_code(q), _default_scale(d, scale),
+          int(bool(causal)), _stream(q.device))
     return dq, dk, dv
 
 

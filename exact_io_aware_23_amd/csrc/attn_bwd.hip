@@ -116,14 +116,17 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int dt, int h, co
   return out;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(256, 2)
 bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                 const float* __restrict__ Lse, const bf16* __restrict__ dO, const float* __restrict__ Delta,
                 bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int n_ktiles, int total, float c,
-                float scale) {
+                float scale, const uint8_t* __restrict__ Mask, int mask_hs, int nb) {
   using C = DkdvCfg<D>;
   __shared__ __attribute__((aligned(16))) char smem[C::BYTES];
+  // block-sparse: the query blocks of this key block whose 128 x 128 block is on
+  __shared__ uint16_t qlist[SPARSE ? kMaxSparseN / C::BQ : 1];
+  __shared__ int wcnt[SPARSE ? 4 : 1];
   bf16* Vs = reinterpret_cast<bf16*>(smem);
   bf16* Xs = Vs + C::V_ELEMS;                                          // stage s: Q at s*STAGE, dO after
   float* Fs = reinterpret_cast<float*>(smem + (C::V_ELEMS + 2 * C::STAGE) * 2);  // stage s: L' [32], delta [32]
@@ -178,7 +181,11 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
       bload16_lds(rQ, Qs + b * 512, qoff[i], q0 * D * 2);
       bload16_lds(rdO, Qs + C::QTILE + b * 512, qoff[i], q0 * D * 2);
     }
-    if (tid < 32) stat = __uint_as_float(bload4(rL, (q0 + tid) * 4, 0)) * kLog2e;
+    if (tid < 32) {
+      // a row with no allowed key (L = -inf) gets p = exp2(-inf) = 0
+      const float lrow = __uint_as_float(bload4(rL, (q0 + tid) * 4, 0));
+      stat = lrow == -INFINITY ? INFINITY : lrow * kLog2e;
+    }
     else if (tid < 64) stat = __uint_as_float(bload4(rD, (q0 + tid - 32) * 4, 0));
   };
   auto store_stat = [&](int stage) {
@@ -202,16 +209,35 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 
   const int n_qt = (N + C::BQ - 1) / C::BQ;
   const int qt_begin = CAUSAL ? (k0 / C::BQ) : 0;
-  if (qt_begin < n_qt) load_q(qt_begin * C::BQ, 0);
+  // the workgroup visits query blocks it_of(0), it_of(1), ... (n_it of them)
+  int n_it = max(n_qt - qt_begin, 0);
+  if constexpr (SPARSE) {
+    // query block t holds rows [32 t, 32 t + 32), in block row t / 4; this is block column kt
+    const uint8_t* mcol = Mask + (size_t)bh * mask_hs + kt;
+    n_it = uniform(compact_indices(qlist, wcnt, qt_begin, n_qt,
+                                   [&](int t) { return mcol[(size_t)(t >> 2) * nb] != 0; }));
+  }
+  auto it_of = [&](int idx) -> int {
+    if constexpr (SPARSE) return uniform((int)qlist[idx]);
+    else return qt_begin + idx;
+  };
+  // first rows of query blocks idx and idx+1, carried from iteration to
+  // iteration; a block-sparse iteration reads the list entry for idx+2 early
+  // and makes it scalar only after its barrier
+  int q_cur = n_it > 0 ? it_of(0) * C::BQ : 0;
+  int q_nxt = n_it > 1 ? it_of(1) * C::BQ : 0;
+  if (n_it > 0) load_q(q_cur, 0);
   wait_vmem_all();
   store_stat(0);
   __syncthreads();
 
-  for (int it = qt_begin; it < n_qt; ++it) {
-    const int stage = (it - qt_begin) & 1;
-    const int q0 = it * C::BQ;
-    const bool has_next = it + 1 < n_qt;
-    if (has_next) load_q(q0 + C::BQ, stage ^ 1);
+  for (int idx = 0; idx < n_it; ++idx) {
+    int raw2 = 0;
+    if constexpr (SPARSE) raw2 = qlist[min(idx + 2, kMaxSparseN / C::BQ - 1)];
+    const int stage = idx & 1;
+    const int q0 = q_cur;
+    const bool has_next = idx + 1 < n_it;
+    if (has_next) load_q(q_nxt, stage ^ 1);
 
     const bool active = kw0 < N && !(CAUSAL && q0 < kw0);
     if (active) {
@@ -272,6 +298,9 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
       store_stat(stage ^ 1);
     }
     __syncthreads();
+    q_cur = q_nxt;
+    if constexpr (SPARSE) q_nxt = idx + 2 < n_it ? uniform(raw2) * C::BQ : 0;
+    else q_nxt = (qt_begin + idx + 2) * C::BQ;
   }
 
   // ---- epilogue: dK = scale * (dK^T)^T, dV = (dV^T)^T
@@ -307,14 +336,17 @@ struct DqCfg {
   static constexpr int STAGE = 2 * TILE;             // K then V, row-major, swizzled
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(256, 2)
 bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
               const float* __restrict__ Lse, const bf16* __restrict__ dO, const float* __restrict__ Delta,
               bf16* __restrict__ dQ, float* __restrict__ DeltaOut, int N, int n_qtiles, int total, float c,
-              float scale) {
+              float scale, const uint8_t* __restrict__ Mask, int mask_hs, int nb) {
   using C = DqCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
+  // block-sparse: the key tiles of this query block whose 128 x 128 block is on
+  __shared__ uint16_t tlist[SPARSE ? kMaxSparseN / C::BC : 1];
+  __shared__ int wcnt[SPARSE ? 4 : 1];
 
   const int work = xcd_remap(blockIdx.x, total);
   const int bh = work / n_qtiles;
@@ -342,15 +374,27 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
     qreg[ks] = __builtin_bit_cast(bf16x8, bload16(rQ, qoff + 32 * ks, 0));
     doreg[ks] = __builtin_bit_cast(bf16x8, bload16(rdO, qoff + 32 * ks, 0));
   }
-  const float lq = q < N ? Lse[(size_t)bh * N + q] * kLog2e : INFINITY;
+  // rows past N, and rows with no allowed key (L = -inf), get p = exp2(-inf) = 0
+  const float lrow = q < N ? Lse[(size_t)bh * N + q] : -INFINITY;
+  const float lq = lrow == -INFINITY ? INFINITY : lrow * kLog2e;
   const float dq_delta = q < N ? Delta[(size_t)bh * N + q] : 0.f;  // rowsum(dO * O), O as stored
   float d_exact = 0.f;  // this lane's share of sum_j P_qj dP_qj
-  wait_vmem_all();
 
   const int kv_end = CAUSAL ? min(N, qt * C::BRQ + C::BRQ) : N;
-  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  int n_tiles = (kv_end + C::BC - 1) / C::BC;
   int wave_tiles = 0;
   if (q0w < N) wave_tiles = CAUSAL ? (min(N, q0w + 32) + C::BC - 1) / C::BC : n_tiles;
+  if constexpr (SPARSE) {
+    // key tile t holds keys [32 t, 32 t + 32), in block t / 4 of the block row qt
+    const uint8_t* mrow = Mask + (size_t)bh * mask_hs + (size_t)qt * nb;
+    n_tiles = uniform(compact_indices(tlist, wcnt, 0, n_tiles, [&](int t) { return mrow[t >> 2] != 0; }));
+    wave_tiles = uniform(count_below(tlist, n_tiles, wave_tiles));
+  }
+  wait_vmem_all();  // Q, dO, L and delta are in registers (the mask loads overlapped them)
+  auto kv0_of = [&](int j) -> int {
+    if constexpr (SPARSE) return uniform((int)tlist[j]) * C::BC;
+    else return j * C::BC;
+  };
 
   // buffer -> LDS copies of the K and V tiles (1 KB block b gets chunk 64 b + lane)
   int toff[C::NB];
@@ -382,14 +426,21 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
       dq[dt][r] = 0.f;
     }
 
-  load_tile(0, 0);
+  // first keys of tiles j and j+1, carried from iteration to iteration; a
+  // block-sparse iteration reads the list entry for j+2 early and makes it
+  // scalar only after its barrier, when no other LDS read is outstanding
+  int kv_cur = n_tiles > 0 ? kv0_of(0) : 0;
+  int kv_nxt = n_tiles > 1 ? kv0_of(1) : 0;
+  if (n_tiles > 0) load_tile(kv_cur, 0);
   wait_vmem_all();
   __syncthreads();
 
   for (int j = 0; j < n_tiles; ++j) {
+    int raw2 = 0;
+    if constexpr (SPARSE) raw2 = tlist[min(j + 2, kMaxSparseN / C::BC - 1)];
     const int stage = j & 1;
-    const int kv0 = j * C::BC;
-    if (j + 1 < n_tiles) load_tile(kv0 + C::BC, stage ^ 1);
+    const int kv0 = kv_cur;
+    if (j + 1 < n_tiles) load_tile(kv_nxt, stage ^ 1);
 
     if (j < wave_tiles) {
       const bf16* Ks = smem + stage * C::STAGE;
@@ -435,6 +486,9 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
 
     wait_vmem_all();  // the next tile has landed in LDS
     __syncthreads();
+    kv_cur = kv_nxt;
+    if constexpr (SPARSE) kv_nxt = j + 2 < n_tiles ? uniform(raw2) * C::BC : 0;
+    else kv_nxt = (j + 2) * C::BC;
   }
 
   // exact delta_q = sum_j P_qj dP_qj, handed to the dK/dV kernel
@@ -460,27 +514,39 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
 
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                         const float* delta, void* dk, void* dv, int BH, int N, float scale,
+                         const float* delta, void* dk, void* dv, int BH, int N, float scale, const BlockMask& m,
                          hipStream_t stream) {
   using C = DkdvCfg<D>;
+  static_assert(C::BKV == kMaskBlock, "a workgroup owns one block column of the mask");
   const int n_kt = (N + C::BKV - 1) / C::BKV;
   const int total = BH * n_kt;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, stream, (const bf16*)q,
-                     (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dk, (bf16*)dv, N,
-                     n_kt, total, scale * kLog2e, scale);
+  if (m.ptr)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3(total), dim3(256), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dk, (bf16*)dv, N,
+                       n_kt, total, scale * kLog2e, scale, m.ptr, m.head_stride, m.nb);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3(total), dim3(256), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dk, (bf16*)dv, N,
+                       n_kt, total, scale * kLog2e, scale, (const uint8_t*)nullptr, 0, 0);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                        const float* delta, void* dq, float* delta_out, int BH, int N, float scale,
-                       hipStream_t stream) {
+                       const BlockMask& m, hipStream_t stream) {
   using C = DqCfg<D>;
+  static_assert(C::BRQ == kMaskBlock, "a workgroup owns one block row of the mask");
   const int n_qt = (N + C::BRQ - 1) / C::BRQ;
   const int total = BH * n_qt;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, stream, (const bf16*)q,
-                     (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dq, delta_out, N, n_qt, total,
-                     scale * kLog2e, scale);
+  if (m.ptr)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), dim3(total), dim3(256), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dq, delta_out, N,
+                       n_qt, total, scale * kLog2e, scale, m.ptr, m.head_stride, m.nb);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false>), dim3(total), dim3(256), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dq, delta_out, N,
+                       n_qt, total, scale * kLog2e, scale, (const uint8_t*)nullptr, 0, 0);
   return hipGetLastError();
 }
 
@@ -501,22 +567,22 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, 
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                            const float* delta, void* dk, void* dv, int BH, int N, int d, float scale,
-                           bool causal, hipStream_t stream) {
+                           bool causal, const BlockMask& m, hipStream_t stream) {
   if (d == 64)
-    return causal ? launch_dkdv_t<64, true>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, stream)
-                  : launch_dkdv_t<64, false>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, stream);
-  return causal ? launch_dkdv_t<128, true>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, stream)
-                : launch_dkdv_t<128, false>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, stream);
+    return causal ? launch_dkdv_t<64, true>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, m, stream)
+                  : launch_dkdv_t<64, false>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, m, stream);
+  return causal ? launch_dkdv_t<128, true>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, m, stream)
+                : launch_dkdv_t<128, false>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, m, stream);
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                          const float* delta, void* dq, float* delta_out, int BH, int N, int d, float scale,
-                         bool causal, hipStream_t stream) {
+                         bool causal, const BlockMask& m, hipStream_t stream) {
   if (d == 64)
-    return causal ? launch_dq_t<64, true>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, stream)
-                  : launch_dq_t<64, false>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, stream);
-  return causal ? launch_dq_t<128, true>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, stream)
-                : launch_dq_t<128, false>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, stream);
+    return causal ? launch_dq_t<64, true>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, stream)
+                  : launch_dq_t<64, false>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, stream);
+  return causal ? launch_dq_t<128, true>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, stream)
+                : launch_dq_t<128, false>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, stream);
 }
 
 }  // namespace attn

@@ -160,4 +160,41 @@ __device__ __forceinline__ int xcd_remap(int wid, int total) {
   return (wid & 7) * (total >> 3) + (wid >> 3);
 }
 
+// ---- block-sparse masks: one byte per 128 x 128 block of (query, key) pairs
+constexpr int kMaskBlock = 128;
+
+// All 256 threads of a workgroup call this with the same arguments.  Writes
+// the indices t in [t_begin, t_end) for which on(t) holds, in increasing
+// order, to list[0 .. count) and returns count.  `wcnt` is 4 ints of LDS.
+template <typename Pred>
+__device__ __forceinline__ int compact_indices(uint16_t* list, int* wcnt, int t_begin, int t_end, Pred on) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int count = 0;
+  for (int base = t_begin; base < t_end; base += 256) {
+    const int t = base + tid;
+    const bool act = t < t_end && on(t);
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(act);
+    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+    if (lane == 0) wcnt[wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int off = count;
+    for (int w = 0; w < 4; ++w) off += w < wave ? wcnt[w] : 0;
+    if (act) list[off + rank] = (uint16_t)t;
+    count += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    __syncthreads();  // the list is complete and wcnt free for the next round
+  }
+  return count;
+}
+
+// Entries of the increasing list[0 .. n) that are below `bound` (one wave).
+__device__ __forceinline__ int count_below(const uint16_t* list, int n, int bound) {
+  const int lane = threadIdx.x & 63;
+  int c = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < n && (int)list[i] < bound));
+  }
+  return c;
+}
+
 }  // namespace attn

@@ -63,12 +63,16 @@ struct FwdCfg {
 // 2^kTau; the result is unchanged (the same m is used for O and l).
 constexpr float kTau = 8.0f;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__(256, 2)
 fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                bf16* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, int total, float c) {
+                bf16* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, int total, float c,
+                const uint8_t* __restrict__ Mask, int mask_hs, int nb) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
+  // block-sparse: the key tiles of this workgroup whose 128 x 128 block is on
+  __shared__ uint16_t tlist[SPARSE ? kMaxSparseN / C::BC : 1];
+  __shared__ int wcnt[SPARSE ? 4 : 1];
 
   const int work = xcd_remap(blockIdx.x, total);
   const int bh = work / n_qtiles;
@@ -90,11 +94,9 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   // ---- tile ranges (all wave-uniform): the workgroup loads n_tiles tiles,
   // this wave computes the first wave_tiles of them
   const int kv_end = CAUSAL ? min(N, qt * C::BR + C::BR) : N;
-  const int n_tiles = (kv_end + C::BC - 1) / C::BC;
+  int n_tiles = (kv_end + C::BC - 1) / C::BC;
   int wave_tiles = 0;
   if (q0w < N) wave_tiles = ((CAUSAL ? min(N, q0w + 32) : N) + C::BC - 1) / C::BC;
-  // tile j needs the mask when it holds keys past N or (causal) past this wave's first row
-  auto needs_mask = [&](int j) { return (j + 1) * C::BC > N || (CAUSAL && (j + 1) * C::BC - 1 > q0w); };
 
   // ---- Q^T operand in registers: lane (l32, g) holds Q[q][16ks + 8g .. +7]
   bf16x8 qreg[C::KS];
@@ -103,6 +105,20 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, bload16(rQ, qoff + 32 * ks, 0));
   }
+  if constexpr (SPARSE) {
+    // (after the Q loads are issued, so the two latencies overlap)
+    // tile t holds keys [64 t, 64 t + 64), in block t / 2 of the block row qt
+    const uint8_t* mrow = Mask + (size_t)bh * mask_hs + (size_t)qt * nb;
+    n_tiles = uniform(compact_indices(tlist, wcnt, 0, n_tiles, [&](int t) { return mrow[t >> 1] != 0; }));
+    wave_tiles = uniform(count_below(tlist, n_tiles, wave_tiles));
+  }
+  // first key of the j-th tile this workgroup visits (past the end: N, all masked)
+  auto kv0_of = [&](int j) -> int {
+    if constexpr (SPARSE) return j < n_tiles ? uniform((int)tlist[j]) * C::BC : N;
+    else return j * C::BC;
+  };
+  // the tile at kv0 needs the mask when it holds keys past N or (causal) past this wave's first row
+  auto needs_mask = [&](int kv0) { return kv0 + C::BC > N || (CAUSAL && kv0 + C::BC - 1 > q0w); };
 
   // K and V tiles go straight into LDS (row-major, XOR-swizzled 16-byte chunks):
   // wave `wave`, instruction i fills 1 KB block (wave * NKLD + i) of the tile.
@@ -113,15 +129,16 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     const int row = idx / C::NCH, cphys = idx % C::NCH;
     kvoff[i] = (row * D + 8 * (cphys ^ chunk_swz<C::NCH>(row))) * 2;
   }
-  auto load_k = [&](int j, int slot) {
+  // copy the K (V) tile whose first key is kv0 into LDS slot `slot`
+  auto load_k = [&](int kv0, int slot) {
     bf16* Ks = smem + slot * C::STAGE;
 #pragma unroll
-    for (int i = 0; i < C::NKLD; ++i) bload16_lds(rK, Ks + (wave * C::NKLD + i) * 512, kvoff[i], j * C::BC * D * 2);
+    for (int i = 0; i < C::NKLD; ++i) bload16_lds(rK, Ks + (wave * C::NKLD + i) * 512, kvoff[i], kv0 * D * 2);
   };
-  auto load_v = [&](int j, int slot) {
+  auto load_v = [&](int kv0, int slot) {
     bf16* Vs = smem + slot * C::STAGE + C::K_ELEMS;
 #pragma unroll
-    for (int i = 0; i < C::NKLD; ++i) bload16_lds(rV, Vs + (wave * C::NKLD + i) * 512, kvoff[i], j * C::BC * D * 2);
+    for (int i = 0; i < C::NKLD; ++i) bload16_lds(rV, Vs + (wave * C::NKLD + i) * 512, kvoff[i], kv0 * D * 2);
   };
 
   // S^T operand reads: K row swap23(l32) of each 32-key half
@@ -172,12 +189,12 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
       }
   };
   // masked scores become -inf (keys past N, and causal keys past the row)
-  auto mask = [&](f32x16 (&st)[2], int j) {
+  auto mask = [&](f32x16 (&st)[2], int kv0) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = j * C::BC + 32 * kb + crow(r, g);
+        const int key = kv0 + 32 * kb + crow(r, g);
         const bool bad = (key >= N) || (CAUSAL && key > q);
         st[kb][r] = bad ? -INFINITY : st[kb][r];
       }
@@ -261,24 +278,34 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   // before the previous barrier.  The scores of tile j+1 are independent of
   // tile j's exponentials, and tile j's P V of tile j+1's max, so each pair
   // sits in one basic block for the scheduler to interleave.
-  load_k(0, 0);
-  load_v(0, 0);
-  if (n_tiles > 1) load_k(1, 1);
+  const int kv_first = kv0_of(0);
+  if (n_tiles > 0) {
+    load_k(kv_first, 0);
+    load_v(kv_first, 0);
+  }
+  if (n_tiles > 1) load_k(kv0_of(1), 1);
   wait_vmem_all();
   __syncthreads();
   f32x16 sa[2], sb[2];
   if (wave_tiles > 0) {
     scores(0, sa);
-    if (needs_mask(0)) mask(sa, 0);
+    if (needs_mask(kv_first)) mask(sa, kv_first);
     rescale(tile_max(sa));
   }
+  // first keys of tiles j+1 and j+2 at the start of step j, carried from step
+  // to step; a block-sparse step reads the entry for j+3 from the LDS list
+  // early and makes it scalar only after its barrier, when no other LDS read
+  // is outstanding
+  int kv_a = kv0_of(1), kv_b = kv0_of(2);
   __syncthreads();  // every wave has read K(0) before K(2) is loaded over it
 
   // `par` = j & 1, passed as a literal so every LDS address is a constant
   // offset from one per-lane base
   auto step = [&](int j, int par, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    if (j + 2 < n_tiles) load_k(j + 2, par);
-    if (j + 1 < n_tiles) load_v(j + 1, par ^ 1);
+    int raw3 = 0;
+    if constexpr (SPARSE) raw3 = tlist[min(j + 3, kMaxSparseN / C::BC - 1)];
+    if (j + 2 < n_tiles) load_k(kv_b, par);
+    if (j + 1 < n_tiles) load_v(kv_a, par ^ 1);
     if (j < wave_tiles) {
       // The scores of tile j+1 are formed even when this wave has no such
       // tile: the slot then holds another K tile (in bounds), every one of
@@ -290,11 +317,14 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
       pv(par, pop);
       pin_a();
       pin_b();
-      if (needs_mask(j + 1)) mask(nxt, j + 1);
+      if (needs_mask(kv_a)) mask(nxt, kv_a);
       if (j + 1 < wave_tiles) rescale(tile_max(nxt));
     }
     wait_vmem_all();  // K(j+2) and V(j+1) have landed in LDS
     __syncthreads();
+    kv_a = kv_b;
+    if constexpr (SPARSE) kv_b = j + 3 < n_tiles ? uniform(raw3) * C::BC : N;
+    else kv_b = (j + 3) * C::BC;
   };
   int j = 0;
   for (; j + 1 < n_tiles; j += 2) {
@@ -303,11 +333,13 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   }
   if (j < n_tiles) step(j, 0, sa, sb);
 
-  // ---- epilogue: O = O_acc / l, L = (m + log2 l) ln 2
+  // ---- epilogue: O = O_acc / l, L = (m + log2 l) ln 2; a row with no allowed
+  // key (possible only under a block mask) gets O = 0 and L = -inf
   const float lt = pair_sum(l_run);
+  const bool empty_row = SPARSE && lt == 0.f;
   if (q < N) {
     bf16* Oh = O + head + (size_t)q * D;
-    const float inv = 1.0f / lt;
+    const float inv = empty_row ? 0.f : 1.0f / lt;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -318,7 +350,7 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         w[1] = pack_bf16x2(oacc[dt][4 * a + 2] * inv, oacc[dt][4 * a + 3] * inv);
         *reinterpret_cast<u32x2*>(Oh + dcol) = w;
       }
-    if (g == 0) L[(size_t)bh * N + q] = (m_run + log2f(lt)) * kLn2;
+    if (g == 0) L[(size_t)bh * N + q] = empty_row ? -INFINITY : (m_run + log2f(lt)) * kLn2;
   }
 }
 
@@ -393,13 +425,19 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
 
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                             int N, float scale, hipStream_t stream) {
+                             int N, float scale, const BlockMask& m, hipStream_t stream) {
   using C = FwdCfg<D>;
+  static_assert(C::BR == kMaskBlock, "a workgroup owns one block row of the mask");
   const int n_qtiles = (N + C::BR - 1) / C::BR;
   const int total = BH * n_qtiles;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, stream,
-                     (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
-                     scale * kLog2e);
+  if (m.ptr)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true>), dim3(total), dim3(256), 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
+                       scale * kLog2e, m.ptr, m.head_stride, m.nb);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false>), dim3(total), dim3(256), 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
+                       scale * kLog2e, (const uint8_t*)nullptr, 0, 0);
   return hipGetLastError();
 }
 
@@ -416,12 +454,12 @@ hipError_t launch_fwd_f32_t(const void* q, const void* k, const void* v, void* o
 }  // namespace
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                      int d, bool bf16_in, float scale, bool causal, hipStream_t stream) {
+                      int d, bool bf16_in, float scale, bool causal, const BlockMask& m, hipStream_t stream) {
   if (bf16_in) {
-    if (d == 64) return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, BH, N, scale, stream)
-                               : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, BH, N, scale, stream);
-    return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, stream)
-                  : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, stream);
+    if (d == 64) return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, BH, N, scale, m, stream)
+                               : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, BH, N, scale, m, stream);
+    return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, m, stream)
+                  : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, m, stream);
   }
   if (d == 64) return causal ? launch_fwd_f32_t<64, true>(q, k, v, o, lse, BH, N, scale, stream)
                              : launch_fwd_f32_t<64, false>(q, k, v, o, lse, BH, N, scale, stream);

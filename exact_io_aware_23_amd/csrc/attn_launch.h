@@ -2,21 +2,33 @@
 // BH = B * H.  Each returns hipGetLastError() after enqueueing on `stream`.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace attn {
 
+// Optional block-sparse mask: one byte per 128 x 128 block, [heads][nb][nb]
+// with nb = ceil(N / 128); head_stride is 0 when one mask serves every head
+// and nb * nb otherwise.  ptr == nullptr means dense.
+constexpr int kMaxSparseN = 65536;  // longest sequence the block-sparse entry points take
+
+struct BlockMask {
+  const uint8_t* ptr = nullptr;
+  int head_stride = 0;
+  int nb = 0;
+};
+
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                      int d, bool bf16_in, float scale, bool causal, hipStream_t stream);
+                      int d, bool bf16_in, float scale, bool causal, const BlockMask& mask, hipStream_t stream);
 
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int BH, int N, int d,
                                  hipStream_t stream);
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                            const void* dout, const float* delta, void* dk, void* dv, int BH, int N,
-                           int d, float scale, bool causal, hipStream_t stream);
+                           int d, float scale, bool causal, const BlockMask& mask, hipStream_t stream);
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                          const void* dout, const float* delta, void* dq, float* delta_out, int BH, int N,
-                         int d, float scale, bool causal, hipStream_t stream);
+                         int d, float scale, bool causal, const BlockMask& mask, hipStream_t stream);
 
 }  // namespace attn

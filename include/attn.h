@@ -39,17 +39,18 @@
 #define EXACT_ATTN_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID = 1,     /* null pointer, non-positive size, bad scale/causal, workspace too small */
-  ATTN_ERR_UNSUPPORTED = 2, /* d or dtype outside the supported set */
+  ATTN_ERR_UNSUPPORTED = 2, /* d, dtype or (block-sparse) N outside the supported set */
   ATTN_ERR_HIP = 3          /* the HIP runtime refused a launch */
 } attn_status_t;
 
@@ -119,6 +120,36 @@ attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const flo
                           const void* dout, const float* delta, void* dq, float* delta_out, int B,
                           int H, int N, int d, attn_dtype_t dtype, float scale, int causal,
                           void* stream);
+
+/* Block-sparse attention.  The FlashAttention talk transcript
+ * (youtube-distilled.com, FThvfkXWqtE), questions after the method part:
+ * the tiled method also takes imposed sparsity, and skips the computation it
+ * removes.  Here the sparsity is a block mask over 128 x 128 blocks of
+ * (query, key) pairs: pair (i, j) takes part iff its block is on, j < N and,
+ * when causal, j <= i.  Kernels skip the tiles of blocks that are off.
+ *   block_mask : device array of uint8, [mask_heads, nb, nb] row-major with
+ *                nb = ceil(N / 128); entry [h][r][c] != 0 switches on the pairs
+ *                of query rows 128 r .. 128 r + 127 and keys 128 c .. 128 c + 127.
+ *                Read only; caller-owned like every other buffer.
+ *   mask_heads : 1 (one mask for every (batch, head) pair) or B * H (one per
+ *                pair, in the [B, H] order of the tensors).
+ * A query row with no allowed key gets O = 0, L = -inf, dQ = 0, and adds
+ * nothing to dK or dV.  Other arguments, layouts and errors are those of
+ * attn_fwd / attn_bwd.  Supported: dtype ATTN_BF16, d in {64, 128},
+ * N <= 65536 (ATTN_ERR_UNSUPPORTED otherwise); a null block_mask or any other
+ * mask_heads is ATTN_ERR_INVALID. */
+attn_status_t attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    const uint8_t* block_mask, int mask_heads, int B, int H, int N, int d,
+                                    attn_dtype_t dtype, float scale, int causal, void* stream);
+
+/* Backward of attn_fwd_block_sparse, with the same mask: preprocess, dq and
+ * dkdv stages as in attn_bwd, each skipping the tiles of blocks that are off.
+ * Workspace: attn_bwd_workspace_bytes(B, H, N, d) bytes, as for attn_bwd. */
+attn_status_t attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                    const uint8_t* block_mask, int mask_heads, void* workspace,
+                                    size_t workspace_bytes, int B, int H, int N, int d, attn_dtype_t dtype,
+                                    float scale, int causal, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* attn_status_string(attn_status_t s);

@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess", "attn_bwd_dkdv",
-        "attn_bwd_dq", "attn_status_string", "attn_abi_version"])
+        "attn_bwd_dq", "attn_status_string", "attn_abi_version", "attn_fwd_block_sparse",
+        "attn_bwd_block_sparse"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -110,6 +111,54 @@ def test_bwd_validation(lib):
     assert lib.attn_bwd_dq(*([FAKE] * 6), None, FAKE, 1, 1, 8, 64, 1, 0.1, 0, None) == INV
     assert lib.attn_bwd_dq(*([FAKE] * 7), None, 1, 1, 8, 64, 1, 0.1, 0, None) == INV
     assert lib.attn_bwd_dq(*([FAKE] * 8), 1, 1, 8, 128, 1, 0.1, 5, None) == INV
+
+
+def test_block_sparse_validation(lib):
+    INV, UNS = binding.ATTN_ERR_INVALID, binding.ATTN_ERR_UNSUPPORTED
+
+    def fwd_s(ptrs=None, mask=FAKE, mh=1, B=1, H=2, N=300, d=64, dtype=1, scale=0.125, causal=0):
+        p = ptrs or [FAKE] * 5
+        return lib.attn_fwd_block_sparse(*p, mask, mh, B, H, N, d, dtype, scale, causal, None)
+
+    for i in range(5):
+        p = [FAKE] * 5
+        p[i] = None
+        assert fwd_s(p) == INV, i
+    assert fwd_s(mask=None) == INV
+    assert fwd_s(mh=0) == INV
+    assert fwd_s(mh=3) == INV  # neither 1 nor B*H = 2
+    assert fwd_s(causal=3) == INV
+    assert fwd_s(scale=0.0) == INV
+    assert fwd_s(N=65536 + 1) == UNS  # longest block-sparse sequence is 65536
+    assert fwd_s(dtype=0) == UNS  # fp32 block-sparse is not provided
+    assert fwd_s(d=80) == UNS
+    ws = lib.attn_bwd_workspace_bytes(1, 2, 300, 64)
+
+    def bwd_s(ptrs=None, mask=FAKE, mh=2, ws_bytes=ws, N=300, d=64, dtype=1):
+        p = ptrs or [FAKE] * 9
+        return lib.attn_bwd_block_sparse(*p, mask, mh, FAKE, ws_bytes, 1, 2, N, d, dtype, 0.125, 1, None)
+
+    for i in range(9):
+        p = [FAKE] * 9
+        p[i] = None
+        assert bwd_s(p) == INV, i
+    assert bwd_s(mask=None) == INV
+    assert bwd_s(mh=4) == INV
+    assert bwd_s(ws_bytes=ws - 1) == INV
+    assert bwd_s(N=70000) == UNS
+    assert bwd_s(dtype=0) == UNS
+
+
+def test_binding_checks_block_mask_shape():
+    import torch
+
+    q = torch.zeros(1, 2, 300, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # CPU tensors are refused before the mask is looked at
+        binding.fwd_block_sparse(q, q, q, torch.ones(3, 3, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        binding._block_mask(torch.ones(2, 2, dtype=torch.uint8), 1, 2, 300)  # nb is 3
+    with pytest.raises(ValueError):
+        binding._block_mask(torch.ones(3, 3, 3, dtype=torch.uint8), 1, 2, 300)  # 3 heads of masks for B*H = 2
 
 
 def test_binding_refuses_cpu_tensors():
