@@ -8,11 +8,13 @@ forward alone.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
                     [--batch B] [--heads H] [--no-cpu-baseline]
-                    [--block-density P]
+                    [--block-density P] [--dropout P]
 
 --block-density P times the block-sparse entry points instead, on a seeded
 random mask over 128 x 128 blocks (each block on with probability P, diagonal
 blocks always on), counting only the allowed (query, key) pairs.
+--dropout P times attn_fwd_dropout + attn_bwd_dropout at rate P (every pair is
+still computed, so the FLOP counts are the dense ones).
 
 Reported:
   value         whole-step attention TFLOP/s, (F_fwd + F_bwd) / t_step, with the
@@ -60,6 +62,7 @@ def parse():
                     help="fwd: time the forward kernel alone (for profiling); copy: a plain 1 GiB device copy "
                          "(calibrates the HBM byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
+    ap.add_argument("--dropout", type=float, default=None, help="time the dropout entry points at this rate")
     ap.add_argument("--block-density", type=float, default=None,
                     help="time attn_fwd_block_sparse + attn_bwd_block_sparse on a random block mask of this density")
     return ap.parse_args()
@@ -181,6 +184,71 @@ def allowed_pairs_per_head(mask: torch.Tensor, N: int, causal: bool) -> torch.Te
     return (mask.to(torch.int64).cpu() * pairs).sum(dim=(1, 2))
 
 
+def bench_dropout(args, w):
+    """Forward + backward with dropout on P; prints one JSON line."""
+    import exact_io_aware_23_amd as A
+
+    dev = torch.device("cuda", 0)
+    inp = W.draw_workload(w, B=w.B, H=w.H)
+    q, k, v, do = (inp[x].to(dev) for x in ("q", "k", "v", "do"))
+    B, H, N, d = q.shape
+    seed = 0x5EED1234ABCD
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(A.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        A.fwd_dropout(q, k, v, args.dropout, seed, scale=w.scale, causal=w.causal, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        A.bwd_dropout(q, k, v, o, lse, do, args.dropout, seed, scale=w.scale, causal=w.causal, workspace=ws, dq=dq,
+                      dk=dk, dv=dv)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    t_fwd = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    t_bwd = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    F_fwd, F_bwd = w.fwd_flops(), w.bwd_flops()
+    achieved = F_fwd / (t_fwd * 1e-3) / 1e12
+    out = {
+        "metric": "attention with dropout TFLOP/s fwd and fwd+bwd",
+        "value": round((F_fwd + F_bwd) / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "pass": "fwd+bwd",
+                   "dropout": args.dropout, "seed": seed},
+        "fwd_tflops": round(achieved, 2),
+        "bwd_tflops": round(F_bwd / (t_bwd * 1e-3) / 1e12, 2),
+        "kernel_ms": {"fwd": round(t_fwd, 4), "bwd (preprocess+dq+dkdv)": round(t_bwd, 4)},
+        "roofline": {"kernel": "fwd", "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(t_fwd, 4)},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def bench_block_sparse(args, w):
     """Forward + backward of block-sparse attention; prints one JSON line."""
     import exact_io_aware_23_amd as A
@@ -274,6 +342,8 @@ def main():
     w = dataclasses.replace(w, B=args.batch or w.B, H=args.heads or w.H)
     if args.block_density is not None:
         return bench_block_sparse(args, w)
+    if args.dropout is not None:
+        return bench_dropout(args, w)
     fwd_only = args.which == "fwd" or not w.backward
     dev = torch.device("cuda", 0)
     inp = W.draw_workload(w, B=w.B, H=w.H)

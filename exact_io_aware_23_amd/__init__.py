@@ -12,11 +12,13 @@ from .binding import (  # noqa: F401
     bwd,
     bwd_block_sparse,
     bwd_dkdv,
+    bwd_dropout,
     bwd_dq,
     bwd_preprocess,
     bwd_workspace_bytes,
     fwd,
     fwd_block_sparse,
+    fwd_dropout,
     load_library,
     status_string,
 )

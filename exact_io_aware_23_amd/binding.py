@@ -21,6 +21,7 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
 _S = ctypes.c_size_t
+_U64 = ctypes.c_uint64
 
 _SIGNATURES = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -32,6 +33,9 @@ _SIGNATURES = {
     "attn_fwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _S, _I, _I, _I, _I, _I, _F,
                                    _I, _P]),
+    "attn_fwd_dropout": (_I, [_P, _P, _P, _P, _P, _F, _U64, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_dropout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _U64, _P, _S, _I, _I, _I, _I, _I, _F, _I,
+                              _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_abi_version": (_I, []),
 }
@@ -198,6 +202,44 @@ def bwd_block_sparse(q, k, v, o, lse, do, block_mask, scale: float | None = None
           do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), m.data_ptr(), m.shape[0],
           workspace.data_ptr(), workspace.numel(), B, H, N, d, _dtype_code(q), _default_scale(d, scale),
           int(bool(causal)), _stream(q.device))
+    return dq, dk, dv
+
+
+def fwd_dropout(q, k, v, p_drop: float, seed: int, scale: float | None = None, causal: bool = False, out=None,
+                lse=None):
+    """attn_fwd_dropout; returns (O, L).  The rate applied is round(256 p_drop) / 256."""
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check("out", out, (B, H, N, d), q.dtype)
+    _check("lse", lse, (B, H, N), torch.float32)
+    _call("attn_fwd_dropout", q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+          float(p_drop), int(seed) & 0xFFFFFFFFFFFFFFFF, B, H, N, d, _dtype_code(q), _default_scale(d, scale),
+          int(bool(causal)), _stream(q.device))
+    return out, lse
+
+
+def bwd_dropout(q, k, v, o, lse, do, p_drop: float, seed: int, scale: float | None = None, causal: bool = False,
+                workspace=None, dq=None, dk=None, dv=None):
+    """attn_bwd_dropout with the forward's p_drop and seed; returns (dQ, dK, dV)."""
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    _check("lse", lse, (B, H, N), torch.float32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    ws_bytes = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _call("attn_bwd_dropout", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+          do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), float(p_drop),
+          int(seed) & 0xFFFFFFFFFFFFFFFF, workspace.data_ptr(), workspace.numel(), B, H, N, d, _dtype_code(q),
+          _default_scale(d, scale), int(bool(causal)), _stream(q.device))
     return dq, dk, dv
 
 

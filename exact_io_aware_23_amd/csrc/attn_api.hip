@@ -37,7 +37,7 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, flo
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   return map_hip(attn::launch_fwd(q, k, v, o, lse, B * H, N, d, dtype == ATTN_BF16, scale, causal != 0,
-                                  attn::BlockMask{}, (hipStream_t)stream));
+                                  attn::BlockMask{}, attn::DropParams{}, (hipStream_t)stream));
 }
 
 namespace {
@@ -70,7 +70,7 @@ attn_status_t attn_bwd_dkdv(const void* q, const void* k, const void* v, const f
   const attn_status_t s = check_bf16_d(d, dtype);
   if (s != ATTN_OK) return s;
   return map_hip(attn::launch_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, B * H, N, d, scale, causal != 0,
-                                       attn::BlockMask{}, (hipStream_t)stream));
+                                       attn::BlockMask{}, attn::DropParams{}, (hipStream_t)stream));
 }
 
 attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
@@ -81,23 +81,24 @@ attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const flo
   const attn_status_t s = check_bf16_d(d, dtype);
   if (s != ATTN_OK) return s;
   return map_hip(attn::launch_bwd_dq(q, k, v, lse, dout, delta, dq, delta_out, B * H, N, d, scale,
-                                     causal != 0, attn::BlockMask{}, (hipStream_t)stream));
+                                     causal != 0, attn::BlockMask{}, attn::DropParams{}, (hipStream_t)stream));
 }
 
 namespace {
 // preprocess -> dq (also writes the exact delta) -> dkdv, with an optional block mask
 attn_status_t bwd_all(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H, int N,
-                      int d, float scale, int causal, const attn::BlockMask& m, void* stream) {
+                      int d, float scale, int causal, const attn::BlockMask& m, const attn::DropParams& dr,
+                      void* stream) {
   float* delta_approx = static_cast<float*>(workspace);
   float* delta_exact = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes(B, H, N));
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = attn::launch_bwd_preprocess(o, dout, delta_approx, B * H, N, d, st);
   if (e != hipSuccess) return ATTN_ERR_HIP;
   e = attn::launch_bwd_dq(q, k, v, lse, dout, delta_approx, dq, delta_exact, B * H, N, d, scale, causal != 0,
-                          m, st);
+                          m, dr, st);
   if (e != hipSuccess) return ATTN_ERR_HIP;
-  e = attn::launch_bwd_dkdv(q, k, v, lse, dout, delta_exact, dk, dv, B * H, N, d, scale, causal != 0, m, st);
+  e = attn::launch_bwd_dkdv(q, k, v, lse, dout, delta_exact, dk, dv, B * H, N, d, scale, causal != 0, m, dr, st);
   return map_hip(e);
 }
 
@@ -105,6 +106,19 @@ attn_status_t bwd_all(const void* q, const void* k, const void* v, const void* o
 attn_status_t check_mask(const uint8_t* mask, int mask_heads, int B, int H, int N) {
   if (!mask || (mask_heads != 1 && mask_heads != B * H)) return ATTN_ERR_INVALID;
   if (N > attn::kMaxSparseN) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+// dropout rate -> byte threshold t = round(256 p); ATTN_OK when t is in [0, 255]
+attn_status_t make_drop(float p_drop, uint64_t seed, attn::DropParams* dr) {
+  if (!std::isfinite(p_drop) || p_drop < 0.f) return ATTN_ERR_INVALID;
+  const double t = std::floor(256.0 * (double)p_drop + 0.5);
+  if (t > 255.0) return ATTN_ERR_INVALID;
+  dr->on = true;
+  dr->t = (uint32_t)t;
+  dr->seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  dr->seed_hi = (uint32_t)(seed >> 32);
+  dr->inv_keep = (float)(256.0 / (256.0 - t));
   return ATTN_OK;
 }
 
@@ -127,7 +141,7 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
   if (s != ATTN_OK) return s;
   if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d)) return ATTN_ERR_INVALID;
   return bwd_all(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, causal, attn::BlockMask{},
-                 stream);
+                 attn::DropParams{}, stream);
 }
 
 attn_status_t attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -139,7 +153,7 @@ attn_status_t attn_fwd_block_sparse(const void* q, const void* k, const void* v,
   if (s == ATTN_OK) s = check_bf16_d(d, dtype);
   if (s != ATTN_OK) return s;
   return map_hip(attn::launch_fwd(q, k, v, o, lse, B * H, N, d, true, scale, causal != 0,
-                                  make_mask(block_mask, mask_heads, N), (hipStream_t)stream));
+                                  make_mask(block_mask, mask_heads, N), attn::DropParams{}, (hipStream_t)stream));
 }
 
 attn_status_t attn_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
@@ -154,7 +168,35 @@ attn_status_t attn_bwd_block_sparse(const void* q, const void* k, const void* v,
   if (s != ATTN_OK) return s;
   if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d)) return ATTN_ERR_INVALID;
   return bwd_all(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, causal,
-                 make_mask(block_mask, mask_heads, N), stream);
+                 make_mask(block_mask, mask_heads, N), attn::DropParams{}, stream);
+}
+
+attn_status_t attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, float p_drop,
+                               uint64_t seed, int B, int H, int N, int d, attn_dtype_t dtype, float scale,
+                               int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  attn::DropParams dr;
+  attn_status_t s = make_drop(p_drop, seed, &dr);
+  if (s == ATTN_OK) s = check_bf16_d(d, dtype);
+  if (s != ATTN_OK) return s;
+  return map_hip(attn::launch_fwd(q, k, v, o, lse, B * H, N, d, true, scale, causal != 0, attn::BlockMask{}, dr,
+                                  (hipStream_t)stream));
+}
+
+attn_status_t attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                               const void* dout, void* dq, void* dk, void* dv, float p_drop, uint64_t seed,
+                               void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                               attn_dtype_t dtype, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  attn::DropParams dr;
+  attn_status_t s = make_drop(p_drop, seed, &dr);
+  if (s == ATTN_OK) s = check_bf16_d(d, dtype);
+  if (s != ATTN_OK) return s;
+  if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d)) return ATTN_ERR_INVALID;
+  return bwd_all(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, H, N, d, scale, causal, attn::BlockMask{}, dr,
+                 stream);
 }
 
 const char* attn_status_string(attn_status_t s) {

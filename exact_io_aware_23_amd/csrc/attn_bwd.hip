@@ -116,13 +116,15 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int dt, int h, co
   return out;
 }
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ void __launch_bounds__(256, 2)
 bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                 const float* __restrict__ Lse, const bf16* __restrict__ dO, const float* __restrict__ Delta,
                 bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int n_ktiles, int total, float c,
-                float scale, const uint8_t* __restrict__ Mask, int mask_hs, int nb) {
+                float scale, const uint8_t* __restrict__ Mask, int mask_hs, int nb, uint32_t drop_t,
+                uint32_t seed_lo, uint32_t seed_hi, float inv_keep) {
   using C = DkdvCfg<D>;
+  static_assert(!(SPARSE && DROP), "block-sparse and dropout are separate entry points");
   __shared__ __attribute__((aligned(16))) char smem[C::BYTES];
   // block-sparse: the query blocks of this key block whose 128 x 128 block is on
   __shared__ uint16_t qlist[SPARSE ? kMaxSparseN / C::BQ : 1];
@@ -266,6 +268,9 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
           s[r] = bad ? -INFINITY : s[r];
         }
       }
+      // dropout: dP = Z dO V^T / (1 - rate) and the dV operand is Z P / (1 - rate)
+      uint32_t keep = 0xFFFFu;
+      if constexpr (DROP) keep = keep_bits_col(key, q0, g, bh, drop_t, seed_lo, seed_hi);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -276,8 +281,15 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
           for (int i = 0; i < 4; ++i) {
             const int r = 8 * h + 4 * v4 + i;
             const float p = fast_exp2(fmaf(s[r], c, -lv[i]));
-            s[r] = p;
-            dp[r] = p * (dp[r] - dv4[i]);
+            if constexpr (DROP) {
+              const bool kept = (keep >> r) & 1u;
+              const float dpr = kept ? dp[r] * inv_keep : 0.f;
+              s[r] = kept ? p * inv_keep : 0.f;
+              dp[r] = p * (dpr - dv4[i]);
+            } else {
+              s[r] = p;
+              dp[r] = p * (dp[r] - dv4[i]);
+            }
           }
         }
       // ---- dV^T += dO^T P and dK^T += Q^T dS (A operands by transposing reads)
@@ -336,13 +348,15 @@ struct DqCfg {
   static constexpr int STAGE = 2 * TILE;             // K then V, row-major, swizzled
 };
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ void __launch_bounds__(256, 2)
 bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
               const float* __restrict__ Lse, const bf16* __restrict__ dO, const float* __restrict__ Delta,
               bf16* __restrict__ dQ, float* __restrict__ DeltaOut, int N, int n_qtiles, int total, float c,
-              float scale, const uint8_t* __restrict__ Mask, int mask_hs, int nb) {
+              float scale, const uint8_t* __restrict__ Mask, int mask_hs, int nb, uint32_t drop_t,
+              uint32_t seed_lo, uint32_t seed_hi, float inv_keep) {
   using C = DqCfg<D>;
+  static_assert(!(SPARSE && DROP), "block-sparse and dropout are separate entry points");
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
   // block-sparse: the key tiles of this query block whose 128 x 128 block is on
   __shared__ uint16_t tlist[SPARSE ? kMaxSparseN / C::BC : 1];
@@ -465,6 +479,11 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
           st[r] = bad ? -INFINITY : st[r];
         }
       }
+      if constexpr (DROP) {  // dP = Z dO V^T / (1 - rate)
+        const uint32_t keep = keep_bits_row(q, kv0, g, bh, drop_t, seed_lo, seed_hi);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dpt[r] = (keep >> r) & 1u ? dpt[r] * inv_keep : 0.f;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(fmaf(st[r], c, -lq));
@@ -515,38 +534,48 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                          const float* delta, void* dk, void* dv, int BH, int N, float scale, const BlockMask& m,
-                         hipStream_t stream) {
+                         const DropParams& dr, hipStream_t stream) {
   using C = DkdvCfg<D>;
   static_assert(C::BKV == kMaskBlock, "a workgroup owns one block column of the mask");
   const int n_kt = (N + C::BKV - 1) / C::BKV;
   const int total = BH * n_kt;
+#define ATTN_DKDV_ARGS                                                                                         \
+  dim3(total), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, \
+      (bf16*)dk, (bf16*)dv, N, n_kt, total, scale * kLog2e, scale
   if (m.ptr)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3(total), dim3(256), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dk, (bf16*)dv, N,
-                       n_kt, total, scale * kLog2e, scale, m.ptr, m.head_stride, m.nb);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true, false>), ATTN_DKDV_ARGS, m.ptr, m.head_stride, m.nb, 0u, 0u,
+                       0u, 1.f);
+  else if (dr.on)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false, true>), ATTN_DKDV_ARGS, (const uint8_t*)nullptr, 0, 0,
+                       dr.t, dr.seed_lo, dr.seed_hi, dr.inv_keep);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false>), dim3(total), dim3(256), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dk, (bf16*)dv, N,
-                       n_kt, total, scale * kLog2e, scale, (const uint8_t*)nullptr, 0, 0);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false, false>), ATTN_DKDV_ARGS, (const uint8_t*)nullptr, 0, 0,
+                       0u, 0u, 0u, 1.f);
+#undef ATTN_DKDV_ARGS
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                        const float* delta, void* dq, float* delta_out, int BH, int N, float scale,
-                       const BlockMask& m, hipStream_t stream) {
+                       const BlockMask& m, const DropParams& dr, hipStream_t stream) {
   using C = DqCfg<D>;
   static_assert(C::BRQ == kMaskBlock, "a workgroup owns one block row of the mask");
   const int n_qt = (N + C::BRQ - 1) / C::BRQ;
   const int total = BH * n_qt;
+#define ATTN_DQ_ARGS                                                                                           \
+  dim3(total), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, \
+      (bf16*)dq, delta_out, N, n_qt, total, scale * kLog2e, scale
   if (m.ptr)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true>), dim3(total), dim3(256), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dq, delta_out, N,
-                       n_qt, total, scale * kLog2e, scale, m.ptr, m.head_stride, m.nb);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true, false>), ATTN_DQ_ARGS, m.ptr, m.head_stride, m.nb, 0u, 0u, 0u,
+                       1.f);
+  else if (dr.on)
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, true>), ATTN_DQ_ARGS, (const uint8_t*)nullptr, 0, 0, dr.t,
+                       dr.seed_lo, dr.seed_hi, dr.inv_keep);
   else
-    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false>), dim3(total), dim3(256), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dq, delta_out, N,
-                       n_qt, total, scale * kLog2e, scale, (const uint8_t*)nullptr, 0, 0);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, false>), ATTN_DQ_ARGS, (const uint8_t*)nullptr, 0, 0, 0u, 0u,
+                       0u, 1.f);
+#undef ATTN_DQ_ARGS
   return hipGetLastError();
 }
 
@@ -567,22 +596,22 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, 
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                            const float* delta, void* dk, void* dv, int BH, int N, int d, float scale,
-                           bool causal, const BlockMask& m, hipStream_t stream) {
+                           bool causal, const BlockMask& m, const DropParams& dr, hipStream_t stream) {
   if (d == 64)
-    return causal ? launch_dkdv_t<64, true>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, m, stream)
-                  : launch_dkdv_t<64, false>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, m, stream);
-  return causal ? launch_dkdv_t<128, true>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, m, stream)
-                : launch_dkdv_t<128, false>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, m, stream);
+    return causal ? launch_dkdv_t<64, true>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, m, dr, stream)
+                  : launch_dkdv_t<64, false>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, m, dr, stream);
+  return causal ? launch_dkdv_t<128, true>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, m, dr, stream)
+                : launch_dkdv_t<128, false>(q, k, v, lse, dout, delta, dk, dv, BH, N, scale, m, dr, stream);
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                          const float* delta, void* dq, float* delta_out, int BH, int N, int d, float scale,
-                         bool causal, const BlockMask& m, hipStream_t stream) {
+                         bool causal, const BlockMask& m, const DropParams& dr, hipStream_t stream) {
   if (d == 64)
-    return causal ? launch_dq_t<64, true>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, stream)
-                  : launch_dq_t<64, false>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, stream);
-  return causal ? launch_dq_t<128, true>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, stream)
-                : launch_dq_t<128, false>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, stream);
+    return causal ? launch_dq_t<64, true>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, dr, stream)
+                  : launch_dq_t<64, false>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, dr, stream);
+  return causal ? launch_dq_t<128, true>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, dr, stream)
+                : launch_dq_t<128, false>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, dr, stream);
 }
 
 }  // namespace attn

@@ -160,6 +160,71 @@ __device__ __forceinline__ int xcd_remap(int wid, int total) {
   return (wid & 7) * (total >> 3) + (wid >> 3);
 }
 
+// ---- dropout decisions: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011)
+// One call maps a 128-bit counter and a 64-bit key to 128 random bits: ten
+// rounds of two 32 x 32 -> 64-bit products, with the key advanced by two Weyl
+// increments before every round after the first.  Element (i, j) of head bh
+// uses the call for counter (j / 4, i / 4, bh, 0), byte 4 (i % 4) + (j % 4)
+// of its four little-endian words, and is kept iff that byte >= t.
+struct Philox4 {
+  uint32_t w[4];
+};
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                 uint32_t k1) {
+#pragma unroll
+  for (int rnd = 0; rnd < 10; ++rnd) {
+    if (rnd > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  return Philox4{{c0, c1, c2, c3}};
+}
+
+// Keep bits of the 16 scores a lane holds in the S^T layout of one 32-key
+// block: the lane owns query row q and register r holds key
+// kb0 + 16 (r / 8) + 8 g + r % 8.  Bit r is set iff that element is kept.
+// Four generator calls (one per 4-key group), word q % 4 of each.
+__device__ __forceinline__ uint32_t keep_bits_row(int q, int kb0, int g, int bh, uint32_t t, uint32_t k0,
+                                                  uint32_t k1) {
+  uint32_t bits = 0;
+  const int wi = q & 3;
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    const uint32_t kg = (uint32_t)(kb0 + 16 * (cc >> 1) + 8 * g + 4 * (cc & 1)) >> 2;
+    const Philox4 w = philox4x32_10(kg, (uint32_t)q >> 2, (uint32_t)bh, 0u, k0, k1);
+    const uint32_t word = wi == 0 ? w.w[0] : wi == 1 ? w.w[1] : wi == 2 ? w.w[2] : w.w[3];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bits |= (((word >> (8 * b)) & 0xFFu) >= t ? 1u : 0u) << (4 * cc + b);
+  }
+  return bits;
+}
+
+// The same for the S layout of one 32-query block: the lane owns key column
+// `key` and register r holds query qb0 + 16 (r / 8) + 8 g + r % 8.  Four calls
+// (one per 4-query group), byte key % 4 of each of their four words.
+__device__ __forceinline__ uint32_t keep_bits_col(int key, int qb0, int g, int bh, uint32_t t, uint32_t k0,
+                                                  uint32_t k1) {
+  uint32_t bits = 0;
+  const int sh = 8 * (key & 3);
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    const uint32_t qg = (uint32_t)(qb0 + 16 * (cc >> 1) + 8 * g + 4 * (cc & 1)) >> 2;
+    const Philox4 w = philox4x32_10((uint32_t)key >> 2, qg, (uint32_t)bh, 0u, k0, k1);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) bits |= (((w.w[b] >> sh) & 0xFFu) >= t ? 1u : 0u) << (4 * cc + b);
+  }
+  return bits;
+}
+
 // ---- block-sparse masks: one byte per 128 x 128 block of (query, key) pairs
 constexpr int kMaskBlock = 128;
 

@@ -63,12 +63,14 @@ struct FwdCfg {
 // 2^kTau; the result is unchanged (the same m is used for O and l).
 constexpr float kTau = 8.0f;
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ void __launch_bounds__(256, 2)
 fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                 bf16* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, int total, float c,
-                const uint8_t* __restrict__ Mask, int mask_hs, int nb) {
+                const uint8_t* __restrict__ Mask, int mask_hs, int nb, uint32_t drop_t, uint32_t seed_lo,
+                uint32_t seed_hi, float inv_keep) {
   using C = FwdCfg<D>;
+  static_assert(!(SPARSE && DROP), "block-sparse and dropout are separate entry points");
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
   // block-sparse: the key tiles of this workgroup whose 128 x 128 block is on
   __shared__ uint16_t tlist[SPARSE ? kMaxSparseN / C::BC : 1];
@@ -221,8 +223,11 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
     }
   };
-  // p = exp2(s c - m) in place, the row sum into l, and the P^T operands
-  auto exps = [&](f32x16 (&st)[2], bf16x8 (&pop)[4]) {
+  // p = exp2(s c - m) in place, the row sum into l, and the P^T operands.
+  // With dropout, l sums every p (L is the logsumexp without dropout) and the
+  // dropped entries become 0 in the P V operand; 1 / (1 - rate) is applied
+  // with the division by l at the end.
+  auto exps = [&](f32x16 (&st)[2], bf16x8 (&pop)[4], int kv0) {
     const float mneg = -m_run;
     float rs = 0.f;
 #pragma unroll
@@ -234,6 +239,14 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         rs += p;
       }
     l_run += rs;
+    if constexpr (DROP) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t keep = keep_bits_row(q, kv0 + 32 * kb, g, bh, drop_t, seed_lo, seed_hi);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[kb][r] = (keep >> r) & 1u ? st[kb][r] : 0.f;
+      }
+    }
 #pragma unroll
     for (int m = 0; m < 4; ++m) pop[m] = c_to_operand(st[m >> 1], m & 1);
   };
@@ -253,7 +266,7 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   // transposing reads and a little VALU.
   constexpr int SM = 2 * C::KS, PVM = 4 * C::DT;  // MFMAs per phase
   auto pin_a = [&]() {
-    constexpr int VA = (120 + SM - 1) / SM;
+    constexpr int VA = ((DROP ? 1100 : 120) + SM - 1) / SM;  // dropout adds its generator calls
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
@@ -313,7 +326,7 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
       // all to -inf, and the rescale is skipped.  One code path per step.
       bf16x8 pop[4];
       scores(par ^ 1, nxt);
-      exps(cur, pop);
+      exps(cur, pop, j * C::BC);  // (dropout runs on dense tiles only, so tile j starts at key 64 j)
       pv(par, pop);
       pin_a();
       pin_b();
@@ -339,7 +352,7 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   const bool empty_row = SPARSE && lt == 0.f;
   if (q < N) {
     bf16* Oh = O + head + (size_t)q * D;
-    const float inv = empty_row ? 0.f : 1.0f / lt;
+    const float inv = empty_row ? 0.f : (DROP ? inv_keep : 1.0f) / lt;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
@@ -425,19 +438,23 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
 
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                             int N, float scale, const BlockMask& m, hipStream_t stream) {
+                             int N, float scale, const BlockMask& m, const DropParams& dr, hipStream_t stream) {
   using C = FwdCfg<D>;
   static_assert(C::BR == kMaskBlock, "a workgroup owns one block row of the mask");
   const int n_qtiles = (N + C::BR - 1) / C::BR;
   const int total = BH * n_qtiles;
   if (m.ptr)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true>), dim3(total), dim3(256), 0, stream,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, false>), dim3(total), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
-                       scale * kLog2e, m.ptr, m.head_stride, m.nb);
+                       scale * kLog2e, m.ptr, m.head_stride, m.nb, 0u, 0u, 0u, 1.f);
+  else if (dr.on)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, true>), dim3(total), dim3(256), 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
+                       scale * kLog2e, (const uint8_t*)nullptr, 0, 0, dr.t, dr.seed_lo, dr.seed_hi, dr.inv_keep);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false>), dim3(total), dim3(256), 0, stream,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, false>), dim3(total), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
-                       scale * kLog2e, (const uint8_t*)nullptr, 0, 0);
+                       scale * kLog2e, (const uint8_t*)nullptr, 0, 0, 0u, 0u, 0u, 1.f);
   return hipGetLastError();
 }
 
@@ -454,12 +471,13 @@ hipError_t launch_fwd_f32_t(const void* q, const void* k, const void* v, void* o
 }  // namespace
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                      int d, bool bf16_in, float scale, bool causal, const BlockMask& m, hipStream_t stream) {
+                      int d, bool bf16_in, float scale, bool causal, const BlockMask& m, const DropParams& dr,
+                      hipStream_t stream) {
   if (bf16_in) {
-    if (d == 64) return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, BH, N, scale, m, stream)
-                               : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, BH, N, scale, m, stream);
-    return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, m, stream)
-                  : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, m, stream);
+    if (d == 64) return causal ? launch_fwd_bf16_t<64, true>(q, k, v, o, lse, BH, N, scale, m, dr, stream)
+                               : launch_fwd_bf16_t<64, false>(q, k, v, o, lse, BH, N, scale, m, dr, stream);
+    return causal ? launch_fwd_bf16_t<128, true>(q, k, v, o, lse, BH, N, scale, m, dr, stream)
+                  : launch_fwd_bf16_t<128, false>(q, k, v, o, lse, BH, N, scale, m, dr, stream);
   }
   if (d == 64) return causal ? launch_fwd_f32_t<64, true>(q, k, v, o, lse, BH, N, scale, stream)
                              : launch_fwd_f32_t<64, false>(q, k, v, o, lse, BH, N, scale, stream);

@@ -17,18 +17,31 @@ struct BlockMask {
   int nb = 0;
 };
 
+// Optional dropout on P: an element is kept iff its generator byte is >= t
+// (rate t / 256); kept entries are scaled by inv_keep = 1 / (1 - t / 256).
+// seed_lo / seed_hi are the two halves of the 64-bit generator key.
+struct DropParams {
+  bool on = false;
+  uint32_t t = 0;
+  uint32_t seed_lo = 0, seed_hi = 0;
+  float inv_keep = 1.f;
+};
+
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                      int d, bool bf16_in, float scale, bool causal, const BlockMask& mask, hipStream_t stream);
+                      int d, bool bf16_in, float scale, bool causal, const BlockMask& mask, const DropParams& drop,
+                      hipStream_t stream);
 
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, float* delta, int BH, int N, int d,
                                  hipStream_t stream);
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                            const void* dout, const float* delta, void* dk, void* dv, int BH, int N,
-                           int d, float scale, bool causal, const BlockMask& mask, hipStream_t stream);
+                           int d, float scale, bool causal, const BlockMask& mask, const DropParams& drop,
+                           hipStream_t stream);
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
                          const void* dout, const float* delta, void* dq, float* delta_out, int BH, int N,
-                         int d, float scale, bool causal, const BlockMask& mask, hipStream_t stream);
+                         int d, float scale, bool causal, const BlockMask& mask, const DropParams& drop,
+                         hipStream_t stream);
 
 }  // namespace attn

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum {
   ATTN_OK = 0,
@@ -150,6 +150,34 @@ attn_status_t attn_bwd_block_sparse(const void* q, const void* k, const void* v,
                                     const uint8_t* block_mask, int mask_heads, void* workspace,
                                     size_t workspace_bytes, int B, int H, int N, int d, attn_dtype_t dtype,
                                     float scale, int causal, void* stream);
+
+/* Attention with dropout on P.  The FlashAttention talk transcript
+ * (youtube-distilled.com, FThvfkXWqtE): standard attention optionally applies
+ * dropout to the softmax output before the product with V, and the fused
+ * kernel drops entries without writing them out, while the gradients use the
+ * same decisions.  Here O = (Z * P / (1 - rate)) V with Z_ij in {0, 1}; L is
+ * the logsumexp without dropout.  Z is regenerated, never stored: element
+ * (i, j) of head bh = b * H + h takes the Philox4x32-10 output (Salmon et
+ * al., SC 2011) for counter (j / 4, i / 4, bh, 0) and key (seed mod 2^32,
+ * seed / 2^32), byte 4 (i % 4) + (j % 4) of its four little-endian words, and
+ * is kept iff that byte >= t with t = round(256 * p_drop); the rate applied
+ * is exactly t / 256.
+ *   p_drop : requested rate, finite, with round(256 p_drop) in [0, 255]
+ *            (ATTN_ERR_INVALID otherwise); 0 gives plain attention.
+ *   seed   : the 64-bit generator key; the backward must get the forward's.
+ * Other arguments, layouts and errors are those of attn_fwd / attn_bwd.
+ * Supported: dtype ATTN_BF16, d in {64, 128}. */
+attn_status_t attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, float p_drop,
+                               uint64_t seed, int B, int H, int N, int d, attn_dtype_t dtype, float scale,
+                               int causal, void* stream);
+
+/* Backward of attn_fwd_dropout with the same p_drop and seed: dV = (Z P / (1 - rate))^T dO,
+ * dP = Z dO V^T / (1 - rate), dS = P (dP - delta), dQ = scale dS K, dK = scale dS^T Q.
+ * Workspace: attn_bwd_workspace_bytes(B, H, N, d) bytes, as for attn_bwd. */
+attn_status_t attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                               const void* dout, void* dq, void* dk, void* dv, float p_drop, uint64_t seed,
+                               void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                               attn_dtype_t dtype, float scale, int causal, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* attn_status_string(attn_status_t s);

@@ -34,7 +34,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess", "attn_bwd_dkdv",
         "attn_bwd_dq", "attn_status_string", "attn_abi_version", "attn_fwd_block_sparse",
-        "attn_bwd_block_sparse"])
+        "attn_bwd_block_sparse", "attn_fwd_dropout", "attn_bwd_dropout"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -147,6 +147,39 @@ def test_block_sparse_validation(lib):
     assert bwd_s(ws_bytes=ws - 1) == INV
     assert bwd_s(N=70000) == UNS
     assert bwd_s(dtype=0) == UNS
+
+
+def test_dropout_validation(lib):
+    INV, UNS = binding.ATTN_ERR_INVALID, binding.ATTN_ERR_UNSUPPORTED
+
+    def fwd_d(ptrs=None, p=0.1, seed=7, N=100, d=64, dtype=1, causal=0):
+        pp = ptrs or [FAKE] * 5
+        return lib.attn_fwd_dropout(*pp, p, seed, 1, 2, N, d, dtype, 0.125, causal, None)
+
+    for i in range(5):
+        pp = [FAKE] * 5
+        pp[i] = None
+        assert fwd_d(pp) == INV, i
+    assert fwd_d(p=-0.01) == INV
+    assert fwd_d(p=float("nan")) == INV
+    assert fwd_d(p=0.999) == INV  # round(256 p) = 256 is past the last threshold
+    assert fwd_d(p=1.0) == INV
+    assert fwd_d(causal=2) == INV
+    assert fwd_d(dtype=0) == UNS
+    assert fwd_d(d=32) == UNS
+    ws = lib.attn_bwd_workspace_bytes(1, 2, 100, 64)
+
+    def bwd_d(ptrs=None, p=0.25, ws_bytes=ws, dtype=1):
+        pp = ptrs or [FAKE] * 9
+        return lib.attn_bwd_dropout(*pp, p, 7, FAKE, ws_bytes, 1, 2, 100, 64, dtype, 0.125, 0, None)
+
+    for i in range(9):
+        pp = [FAKE] * 9
+        pp[i] = None
+        assert bwd_d(pp) == INV, i
+    assert bwd_d(p=2.0) == INV
+    assert bwd_d(ws_bytes=ws - 1) == INV
+    assert bwd_d(dtype=0) == UNS
 
 
 def test_binding_checks_block_mask_shape():
