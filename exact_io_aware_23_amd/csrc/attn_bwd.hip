@@ -269,8 +269,13 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         }
       }
       // dropout: dP = Z dO V^T / (1 - rate) and the dV operand is Z P / (1 - rate)
-      uint32_t keep = 0xFFFFu;
-      if constexpr (DROP) keep = keep_bits_col(key, q0, g, bh, drop_t, seed_lo, seed_hi);
+      bool kept[16];
+      if constexpr (DROP) {
+        uint32_t word[4];
+        drop_words_col(key, q0, g, bh, seed_lo, seed_hi, word);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) kept[r] = drop_keep(word, r, drop_t);
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -282,9 +287,8 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
             const int r = 8 * h + 4 * v4 + i;
             const float p = fast_exp2(fmaf(s[r], c, -lv[i]));
             if constexpr (DROP) {
-              const bool kept = (keep >> r) & 1u;
-              const float dpr = kept ? dp[r] * inv_keep : 0.f;
-              s[r] = kept ? p * inv_keep : 0.f;
+              const float dpr = kept[r] ? dp[r] * inv_keep : 0.f;
+              s[r] = kept[r] ? p * inv_keep : 0.f;
               dp[r] = p * (dpr - dv4[i]);
             } else {
               s[r] = p;
@@ -480,9 +484,10 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
         }
       }
       if constexpr (DROP) {  // dP = Z dO V^T / (1 - rate)
-        const uint32_t keep = keep_bits_row(q, kv0, g, bh, drop_t, seed_lo, seed_hi);
+        uint32_t word[4];
+        drop_words_row(q, kv0, g, bh, seed_lo, seed_hi, word);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dpt[r] = (keep >> r) & 1u ? dpt[r] * inv_keep : 0.f;
+        for (int r = 0; r < 16; ++r) dpt[r] = drop_keep(word, r, drop_t) ? dpt[r] * inv_keep : 0.f;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {

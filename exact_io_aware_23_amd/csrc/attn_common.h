@@ -189,40 +189,66 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
   return Philox4{{c0, c1, c2, c3}};
 }
 
-// Keep bits of the 16 scores a lane holds in the S^T layout of one 32-key
-// block: the lane owns query row q and register r holds key
-// kb0 + 16 (r / 8) + 8 g + r % 8.  Bit r is set iff that element is kept.
-// Four generator calls (one per 4-key group), word q % 4 of each.
-__device__ __forceinline__ uint32_t keep_bits_row(int q, int kb0, int g, int bh, uint32_t t, uint32_t k0,
-                                                  uint32_t k1) {
-  uint32_t bits = 0;
-  const int wi = q & 3;
+// Lane i of every quad of lanes reads the value of lane i ^ K (DPP quad_perm).
+template <int K>
+__device__ __forceinline__ uint32_t quad_xor(uint32_t v) {
+  constexpr int ctrl = K == 1 ? 0xB1 : K == 2 ? 0x4E : 0x1B;  // [1,0,3,2], [2,3,0,1], [3,2,1,0]
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t pick4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, int i) {
+  return i == 0 ? a0 : i == 1 ? a1 : i == 2 ? a2 : a3;
+}
+
+// Dropout words for the 16 scores a lane holds in the S^T layout of one
+// 32-key block: the lane owns query row q (q % 4 == lane % 4) and register r
+// holds key kb0 + 16 (r / 8) + 8 g + r % 8.  On return word[c] is word q % 4
+// of the generator call for keys kb0 + 16 (c / 2) + 8 g + 4 (c % 2) .. + 3, so
+// register r is kept iff byte r % 4 of word[r / 4] is >= t.  The four lanes of
+// a quad share query group q / 4 and need the same four calls: lane m makes
+// call m and the quad exchanges words (lane n takes word n of each).  Every
+// lane of the quad must be active.
+__device__ __forceinline__ void drop_words_row(int q, int kb0, int g, int bh, uint32_t k0, uint32_t k1,
+                                               uint32_t (&word)[4]) {
+  const int m = threadIdx.x & 3;
+  const uint32_t kg = (uint32_t)(kb0 + 16 * (m >> 1) + 8 * g + 4 * (m & 1)) >> 2;
+  const Philox4 w = philox4x32_10(kg, (uint32_t)q >> 2, (uint32_t)bh, 0u, k0, k1);
+  const uint32_t own = pick4(w.w[0], w.w[1], w.w[2], w.w[3], m);
+  const uint32_t r1 = quad_xor<1>(pick4(w.w[0], w.w[1], w.w[2], w.w[3], m ^ 1));
+  const uint32_t r2 = quad_xor<2>(pick4(w.w[0], w.w[1], w.w[2], w.w[3], m ^ 2));
+  const uint32_t r3 = quad_xor<3>(pick4(w.w[0], w.w[1], w.w[2], w.w[3], m ^ 3));
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
-    const uint32_t kg = (uint32_t)(kb0 + 16 * (cc >> 1) + 8 * g + 4 * (cc & 1)) >> 2;
-    const Philox4 w = philox4x32_10(kg, (uint32_t)q >> 2, (uint32_t)bh, 0u, k0, k1);
-    const uint32_t word = wi == 0 ? w.w[0] : wi == 1 ? w.w[1] : wi == 2 ? w.w[2] : w.w[3];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) bits |= (((word >> (8 * b)) & 0xFFu) >= t ? 1u : 0u) << (4 * cc + b);
-  }
-  return bits;
+  for (int c = 0; c < 4; ++c) word[c] = pick4(own, r1, r2, r3, c ^ m);  // call c came from lane c
 }
 
 // The same for the S layout of one 32-query block: the lane owns key column
-// `key` and register r holds query qb0 + 16 (r / 8) + 8 g + r % 8.  Four calls
-// (one per 4-query group), byte key % 4 of each of their four words.
-__device__ __forceinline__ uint32_t keep_bits_col(int key, int qb0, int g, int bh, uint32_t t, uint32_t k0,
-                                                  uint32_t k1) {
-  uint32_t bits = 0;
-  const int sh = 8 * (key & 3);
+// `key` (key % 4 == lane % 4) and register r holds query qb0 + 16 (r / 8) +
+// 8 g + r % 8.  On return byte w of word[c] is byte key % 4 of word w of the
+// call for queries qb0 + 16 (c / 2) + 8 g + 4 (c % 2) .. + 3, so register r
+// is kept iff byte r % 4 of word[r / 4] is >= t.  Lane m makes call m and
+// sends lane n the bytes n of its four words, packed by v_perm_b32.
+__device__ __forceinline__ void drop_words_col(int key, int qb0, int g, int bh, uint32_t k0, uint32_t k1,
+                                               uint32_t (&word)[4]) {
+  const int m = threadIdx.x & 3;
+  const uint32_t qg = (uint32_t)(qb0 + 16 * (m >> 1) + 8 * g + 4 * (m & 1)) >> 2;
+  const Philox4 w = philox4x32_10((uint32_t)key >> 2, qg, (uint32_t)bh, 0u, k0, k1);
+  // bytes n of w0, w1, w2, w3 -> one word (selector 12 gives a zero byte)
+  auto gather = [&](int n) {
+    const uint32_t sel = (uint32_t)n | ((uint32_t)(4 + n) << 8) | 0x0C0C0000u;
+    const uint32_t lo = __builtin_amdgcn_perm(w.w[1], w.w[0], sel);
+    const uint32_t hi = __builtin_amdgcn_perm(w.w[3], w.w[2], sel);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+  };
+  const uint32_t own = gather(m);
+  const uint32_t r1 = quad_xor<1>(gather(m ^ 1));
+  const uint32_t r2 = quad_xor<2>(gather(m ^ 2));
+  const uint32_t r3 = quad_xor<3>(gather(m ^ 3));
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
-    const uint32_t qg = (uint32_t)(qb0 + 16 * (cc >> 1) + 8 * g + 4 * (cc & 1)) >> 2;
-    const Philox4 w = philox4x32_10((uint32_t)key >> 2, qg, (uint32_t)bh, 0u, k0, k1);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) bits |= (((w.w[b] >> sh) & 0xFFu) >= t ? 1u : 0u) << (4 * cc + b);
-  }
-  return bits;
+  for (int c = 0; c < 4; ++c) word[c] = pick4(own, r1, r2, r3, c ^ m);
+}
+
+// keep decision of register r from the words above
+__device__ __forceinline__ bool drop_keep(const uint32_t (&word)[4], int r, uint32_t t) {
+  return ((word[r >> 2] >> (8 * (r & 3))) & 0xFFu) >= t;
 }
 
 // ---- block-sparse masks: one byte per 128 x 128 block of (query, key) pairs

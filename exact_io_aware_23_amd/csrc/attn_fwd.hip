@@ -242,9 +242,10 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     if constexpr (DROP) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t keep = keep_bits_row(q, kv0 + 32 * kb, g, bh, drop_t, seed_lo, seed_hi);
+        uint32_t word[4];
+        drop_words_row(q, kv0 + 32 * kb, g, bh, seed_lo, seed_hi, word);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st[kb][r] = (keep >> r) & 1u ? st[kb][r] : 0.f;
+        for (int r = 0; r < 16; ++r) st[kb][r] = drop_keep(word, r, drop_t) ? st[kb][r] : 0.f;
       }
     }
 #pragma unroll
@@ -266,7 +267,7 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   // transposing reads and a little VALU.
   constexpr int SM = 2 * C::KS, PVM = 4 * C::DT;  // MFMAs per phase
   auto pin_a = [&]() {
-    constexpr int VA = ((DROP ? 1100 : 120) + SM - 1) / SM;  // dropout adds its generator calls
+    constexpr int VA = ((DROP ? 400 : 120) + SM - 1) / SM;  // dropout adds its generator calls
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i < SM; ++i) {
