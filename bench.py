@@ -8,13 +8,16 @@ forward alone.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
                     [--batch B] [--heads H] [--no-cpu-baseline]
-                    [--block-density P] [--dropout P]
+                    [--block-density P] [--dropout P] [--decode NQ [--decode-nk NK]]
 
 --block-density P times the block-sparse entry points instead, on a seeded
 random mask over 128 x 128 blocks (each block on with probability P, diagonal
 blocks always on), counting only the allowed (query, key) pairs.
 --dropout P times attn_fwd_dropout + attn_bwd_dropout at rate P (every pair is
 still computed, so the FLOP counts are the dense ones).
+--decode NQ times attn_decode: NQ new queries per head against a KV cache of
+--decode-nk keys (B=4, H=32, d=128 unless --batch/--heads say otherwise),
+priced against HBM bandwidth (it reads each cached key and value once).
 
 Reported:
   value         whole-step attention TFLOP/s, (F_fwd + F_bwd) / t_step, with the
@@ -63,6 +66,8 @@ def parse():
                          "(calibrates the HBM byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
     ap.add_argument("--dropout", type=float, default=None, help="time the dropout entry points at this rate")
+    ap.add_argument("--decode", type=int, default=None, help="time attn_decode with this many queries per head")
+    ap.add_argument("--decode-nk", type=int, default=16384, help="cached keys per head for --decode")
     ap.add_argument("--block-density", type=float, default=None,
                     help="time attn_fwd_block_sparse + attn_bwd_block_sparse on a random block mask of this density")
     return ap.parse_args()
@@ -182,6 +187,63 @@ def allowed_pairs_per_head(mask: torch.Tensor, N: int, causal: bool) -> torch.Te
         tri = size * (size + 1) // 2
         pairs = torch.where(c < r, pairs, torch.where(c == r, torch.diag(tri), torch.zeros_like(pairs)))
     return (mask.to(torch.int64).cpu() * pairs).sum(dim=(1, 2))
+
+
+def bench_decode(args):
+    """Decode against a KV cache; prints one JSON line with the HBM roofline."""
+    import exact_io_aware_23_amd as A
+
+    B, H, Nq, Nk, d = args.batch or 4, args.heads or 32, args.decode, args.decode_nk, 128
+    dev = torch.device("cuda", 0)
+    cache = W.draw(B, H, Nk, d, "bf16", seed=6000, backward=False)
+    q = W.draw(B, H, Nq, d, "bf16", seed=6001, backward=False)["q"].to(dev)
+    k, v = cache["k"].to(dev), cache["v"].to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(A.decode_workspace_bytes(B, H, Nq, Nk, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    scale = 1 / (d ** 0.5)
+
+    def step():
+        A.decode(q, k, v, scale=scale, causal=True, out=o, lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        step()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    t_gpu = ev[0].elapsed_time(ev[1]) / args.steps
+    # algorithmic bytes: K and V once, q in, O and L out
+    bytes_ = 2.0 * B * H * Nk * d * 2 + 2.0 * B * H * Nq * d * 2 + 4.0 * B * H * Nq
+    gbs = bytes_ / (t_gpu * 1e-3) / 1e9
+    out = {
+        "metric": "decode attention GB/s against a KV cache (HBM roofline)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode", "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "causal": True},
+        "gpu_ms_per_call": round(t_gpu, 4),
+        "tflops": round(4.0 * d * Nq * Nk * B * H / (t_gpu * 1e-3) / 1e12, 3),
+        "roofline": {"kernel": "decode (partial + merge)", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(t_gpu, 4)},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 def bench_dropout(args, w):
@@ -344,6 +406,8 @@ def main():
         return bench_block_sparse(args, w)
     if args.dropout is not None:
         return bench_dropout(args, w)
+    if args.decode is not None:
+        return bench_decode(args)
     fwd_only = args.which == "fwd" or not w.backward
     dev = torch.device("cuda", 0)
     inp = W.draw_workload(w, B=w.B, H=w.H)

@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     bwd_dq,
     bwd_preprocess,
     bwd_workspace_bytes,
+    decode,
+    decode_workspace_bytes,
     fwd,
     fwd_block_sparse,
     fwd_dropout,

@@ -36,6 +36,8 @@ _SIGNATURES = {
     "attn_fwd_dropout": (_I, [_P, _P, _P, _P, _P, _F, _U64, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_dropout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _F, _U64, _P, _S, _I, _I, _I, _I, _I, _F, _I,
                               _P]),
+    "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
+    "attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_abi_version": (_I, []),
 }
@@ -241,6 +243,31 @@ def bwd_dropout(q, k, v, o, lse, do, p_drop: float, seed: int, scale: float | No
           int(seed) & 0xFFFFFFFFFFFFFFFF, workspace.data_ptr(), workspace.numel(), B, H, N, d, _dtype_code(q),
           _default_scale(d, scale), int(bool(causal)), _stream(q.device))
     return dq, dk, dv
+
+
+def decode_workspace_bytes(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    return int(load_library().attn_decode_workspace_bytes(B, H, Nq, Nk, d))
+
+
+def decode(q, k_cache, v_cache, scale: float | None = None, causal: bool = False, out=None, lse=None,
+           workspace=None):
+    """attn_decode: q [B, H, Nq, d] against the cache [B, H, Nk, d]; returns (O [B, H, Nq, d], L [B, H, Nq])."""
+    B, H, Nq, d = q.shape
+    Nk = k_cache.shape[2]
+    _check("q", q, (B, H, Nq, d), q.dtype)
+    _check("k_cache", k_cache, (B, H, Nk, d), q.dtype)
+    _check("v_cache", v_cache, (B, H, Nk, d), q.dtype)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check("out", out, (B, H, Nq, d), q.dtype)
+    _check("lse", lse, (B, H, Nq), torch.float32)
+    ws_bytes = decode_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _call("attn_decode", q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(), lse.data_ptr(),
+          workspace.data_ptr(), workspace.numel(), B, H, Nq, Nk, d, _dtype_code(q), _default_scale(d, scale),
+          int(bool(causal)), _stream(q.device))
+    return out, lse
 
 
 def bwd_preprocess(o, do, delta=None):

@@ -199,6 +199,29 @@ attn_status_t attn_bwd_dropout(const void* q, const void* k, const void* v, cons
                  stream);
 }
 
+size_t attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 0;
+  if (Nq > attn::decode_max_queries() || Nk > (1 << 23) || (int64_t)B * H * Nk >= ((int64_t)1 << 31)) return 0;
+  const size_t parts = (size_t)B * H * attn::decode_chunks(Nk) * Nq;
+  const size_t bytes = parts * (2 + (size_t)d) * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
+                          attn_dtype_t dtype, float scale, int causal, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || !lse || !workspace) return ATTN_ERR_INVALID;
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (int64_t)B * H * Nk >= ((int64_t)1 << 31)) return ATTN_ERR_INVALID;
+  if (!scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  if (causal && Nq > Nk) return ATTN_ERR_INVALID;
+  if (Nq > attn::decode_max_queries() || Nk > (1 << 23)) return ATTN_ERR_UNSUPPORTED;  // 32-bit byte offsets
+  const attn_status_t s = check_bf16_d(d, dtype);
+  if (s != ATTN_OK) return s;
+  if (workspace_bytes < attn_decode_workspace_bytes(B, H, Nq, Nk, d)) return ATTN_ERR_INVALID;
+  return map_hip(attn::launch_decode(q, k_cache, v_cache, o, lse, static_cast<float*>(workspace), B * H, Nq, Nk,
+                                     d, scale, causal != 0, (hipStream_t)stream));
+}
+
 const char* attn_status_string(attn_status_t s) {
   switch (s) {
     case ATTN_OK: return "ok";

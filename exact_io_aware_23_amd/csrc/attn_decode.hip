@@ -1,0 +1,216 @@
+// Decode attention against a KV cache for gfx950.
+//
+// What it computes (the pages, by title and section): "What is Flash
+// Attention?" (iania.ai video page, English) lists memory-bound inference
+// with long prompts among the uses (10:00) and names the KV cache for fast
+// generation as the next step (11:02-11:33).  A few new queries (Nq <= 8)
+// attend to the Nk keys and values held in a cache; with the causal flag
+// query i is the (Nk - Nq + i)-th position and sees keys j <= Nk - Nq + i.
+//
+// Design (MI355X): decode reads every cached key and value once and does
+// ~2 FLOPs per byte, so it is bound by HBM bandwidth, not by the matrix
+// cores.  The work is split over the keys:
+//   * decode_partial_kernel: one workgroup per (batch*head, 512-key chunk).
+//     Four threads per key form the chunk's scores for every query (16-byte
+//     loads of K, partial dot products against q in LDS, two DPP adds); one
+//     wave per query takes the chunk max and exp-sum; then 16 (d=128) or 32
+//     (d=64) key lanes accumulate sum_j p_j V_j with 16-byte loads of V, and
+//     the lanes and waves are reduced through cross-lane swaps and LDS.  The
+//     chunk's (m, l, unnormalised O) go to the workspace.
+//   * decode_merge_kernel: per (batch*head, query) it merges the chunks with
+//     the online-softmax rule of the same page (04:46-05:17): m = max m_c,
+//     l = sum 2^(m_c - m) l_c, O = sum 2^(m_c - m) O_c / l.
+// Scores are kept in base-2 units (scale * log2 e folded in), as in the
+// forward kernel.
+#include "attn_common.h"
+#include "attn_launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int kDecChunk = 512;  // keys per workgroup
+constexpr int kDecTile = 64;    // keys per pass-1 tile (4 threads per key)
+constexpr int kDecMaxQ = 8;     // most queries per call
+
+template <int D>
+__global__ void __launch_bounds__(256)
+decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                      float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, int Nk, int nq,
+                      int S, float c, int causal) {
+  constexpr int DP = D / 4;          // dims per thread in pass 1
+  constexpr int G8 = D / 8;          // 8-dim groups in pass 2
+  constexpr int KL = 256 / G8;       // key lanes in pass 2
+  __shared__ __attribute__((aligned(16))) float qs[kDecMaxQ][D];
+  __shared__ float sc[kDecMaxQ][kDecChunk];
+  __shared__ __attribute__((aligned(16))) float red[4][kDecMaxQ][D];
+
+  const int bh = blockIdx.x / S;
+  const int s = blockIdx.x % S;
+  const int k0 = s * kDecChunk;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint32_t head_bytes = (uint32_t)Nk * D * 2;
+  const rsrc_t rK = make_rsrc(K + (size_t)bh * Nk * D, head_bytes);
+  const rsrc_t rV = make_rsrc(V + (size_t)bh * Nk * D, head_bytes);
+
+  for (int idx = tid; idx < nq * D; idx += 256) qs[idx / D][idx % D] = (float)Q[(size_t)bh * nq * D + idx];
+  __syncthreads();
+
+  // ---- pass 1: scores of the chunk, in base-2 units; masked keys get -inf
+  {
+    const int kl = tid >> 2, part = tid & 3;
+#pragma unroll 2
+    for (int kt = 0; kt < kDecChunk; kt += kDecTile) {
+      const int key = k0 + kt + kl;
+      float kv[DP];
+#pragma unroll
+      for (int i = 0; i < DP / 8; ++i) {
+        const u32x4 raw = bload16(rK, (key * D + part * DP + 8 * i) * 2, 0);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, raw);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kv[8 * i + e] = (float)b[e];
+      }
+#pragma unroll
+      for (int qi = 0; qi < kDecMaxQ; ++qi) {
+        if (qi >= nq) break;
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < DP; e += 4) {
+          const f32x4 qv = *reinterpret_cast<const f32x4*>(&qs[qi][part * DP + e]);
+          acc = fmaf(kv[e], qv[0], acc);
+          acc = fmaf(kv[e + 1], qv[1], acc);
+          acc = fmaf(kv[e + 2], qv[2], acc);
+          acc = fmaf(kv[e + 3], qv[3], acc);
+        }
+        acc += __builtin_bit_cast(float, quad_xor<1>(__builtin_bit_cast(uint32_t, acc)));
+        acc += __builtin_bit_cast(float, quad_xor<2>(__builtin_bit_cast(uint32_t, acc)));
+        const bool ok = key < Nk && (!causal || key <= Nk - nq + qi);
+        if (part == 0) sc[qi][kt + kl] = ok ? acc * c : -INFINITY;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- chunk max and exp-sum per query (one wave per query); p in place
+  for (int qi = wave; qi < nq; qi += 4) {
+    float m = -INFINITY;
+    for (int i = lane; i < kDecChunk; i += 64) m = fmaxf(m, sc[qi][i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float l = 0.f;
+    for (int i = lane; i < kDecChunk; i += 64) {
+      const float p = m == -INFINITY ? 0.f : fast_exp2(sc[qi][i] - m);
+      sc[qi][i] = p;
+      l += p;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+    if (lane == 0) {
+      ws_m[((size_t)bh * S + s) * nq + qi] = m;
+      ws_l[((size_t)bh * S + s) * nq + qi] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- pass 2: unnormalised O_c = sum_j p_j V_j over the chunk
+  const int g8 = tid % G8, kl2 = tid / G8;
+  float acc[kDecMaxQ][8];
+#pragma unroll
+  for (int qi = 0; qi < kDecMaxQ; ++qi)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[qi][e] = 0.f;
+#pragma unroll 4
+  for (int kj = kl2; kj < kDecChunk; kj += KL) {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, bload16(rV, ((k0 + kj) * D + 8 * g8) * 2, 0));
+    float vv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vv[e] = (float)b[e];
+#pragma unroll
+    for (int qi = 0; qi < kDecMaxQ; ++qi) {
+      if (qi >= nq) break;
+      const float p = sc[qi][kj];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[qi][e] = fmaf(p, vv[e], acc[qi][e]);
+    }
+  }
+  // lanes of one wave with the same g8 hold different keys: fold them
+#pragma unroll
+  for (int qi = 0; qi < kDecMaxQ; ++qi) {
+    if (qi >= nq) break;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = acc[qi][e];
+#pragma unroll
+      for (int off = G8; off < 64; off <<= 1) x += __shfl_xor(x, off);
+      acc[qi][e] = x;
+    }
+  }
+  if (lane < G8) {
+#pragma unroll
+    for (int qi = 0; qi < kDecMaxQ; ++qi) {
+      if (qi >= nq) break;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[wave][qi][8 * g8 + e] = acc[qi][e];
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nq * D; idx += 256) {
+    const int qi = idx / D, dd = idx % D;
+    const float o = red[0][qi][dd] + red[1][qi][dd] + red[2][qi][dd] + red[3][qi][dd];
+    ws_o[(((size_t)bh * S + s) * nq + qi) * D + dd] = o;
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(D)
+decode_merge_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l, const float* __restrict__ ws_o,
+                    bf16* __restrict__ O, float* __restrict__ L, int nq, int S) {
+  const int bh = blockIdx.x / nq, qi = blockIdx.x % nq;
+  const int dd = threadIdx.x;
+  float m = -INFINITY;
+  for (int s = 0; s < S; ++s) m = fmaxf(m, ws_m[((size_t)bh * S + s) * nq + qi]);
+  float l = 0.f, o = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const size_t p = ((size_t)bh * S + s) * nq + qi;
+      const float ms = ws_m[p];
+      if (ms == -INFINITY) continue;
+      const float a = fast_exp2(ms - m);
+      l = fmaf(a, ws_l[p], l);
+      o = fmaf(a, ws_o[p * D + dd], o);
+    }
+  }
+  const bool empty = l == 0.f;
+  O[((size_t)bh * nq + qi) * D + dd] = (bf16)(empty ? 0.f : o / l);
+  if (dd == 0) L[(size_t)bh * nq + qi] = empty ? -INFINITY : (m + log2f(l)) * kLn2;
+}
+
+}  // namespace
+
+int decode_chunks(int Nk) { return (Nk + kDecChunk - 1) / kDecChunk; }
+int decode_max_queries() { return kDecMaxQ; }
+
+hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, float* ws, int BH,
+                         int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream) {
+  const int S = decode_chunks(Nk);
+  const size_t parts = (size_t)BH * S * Nq;
+  float* ws_m = ws;
+  float* ws_l = ws + parts;
+  float* ws_o = ws + 2 * parts;
+  const float c = scale * kLog2e;
+  if (d == 64) {
+    hipLaunchKernelGGL((decode_partial_kernel<64>), dim3(BH * S), dim3(256), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, ws_m, ws_l, ws_o, Nk, Nq, S, c, (int)causal);
+    hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(BH * Nq), dim3(64), 0, stream, ws_m, ws_l, ws_o, (bf16*)o,
+                       lse, Nq, S);
+  } else {
+    hipLaunchKernelGGL((decode_partial_kernel<128>), dim3(BH * S), dim3(256), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, ws_m, ws_l, ws_o, Nk, Nq, S, c, (int)causal);
+    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(BH * Nq), dim3(128), 0, stream, ws_m, ws_l, ws_o,
+                       (bf16*)o, lse, Nq, S);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace attn

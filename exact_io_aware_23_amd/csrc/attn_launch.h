@@ -44,4 +44,13 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const floa
                          int d, float scale, bool causal, const BlockMask& mask, const DropParams& drop,
                          hipStream_t stream);
 
+// Decode against a KV cache: Nq <= decode_max_queries() queries per
+// (batch, head), Nk cached keys, split into decode_chunks(Nk) chunks whose
+// partial results (m, l: BH*S*Nq floats each, then O: BH*S*Nq*d floats) live
+// in the fp32 workspace `ws`.
+int decode_chunks(int Nk);
+int decode_max_queries();
+hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, float* ws, int BH,
+                         int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream);
+
 }  // namespace attn

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 typedef enum {
   ATTN_OK = 0,
@@ -178,6 +178,28 @@ attn_status_t attn_bwd_dropout(const void* q, const void* k, const void* v, cons
                                const void* dout, void* dq, void* dk, void* dv, float p_drop, uint64_t seed,
                                void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                                attn_dtype_t dtype, float scale, int causal, void* stream);
+
+/* Decode against a KV cache.  "What is Flash Attention?" (iania.ai video
+ * page, English): memory-bound inference with long prompts (10:00) and the KV
+ * cache for fast generation (11:02-11:33).  Nq new queries per (batch, head)
+ * attend to the Nk keys and values held in the cache:
+ *     O = softmax(scale q K^T + mask) V,  L = logsumexp per query row.
+ * causal = 1 places the queries at the last Nq positions (query i sees keys
+ * j <= Nk - Nq + i); causal = 0 lets every query see all Nk keys.  The keys
+ * are split into chunks whose partial results are merged with the online
+ * softmax rule of the same page (04:46-05:17).
+ *   q          : [B, H, Nq, d] bf16        o   : output [B, H, Nq, d] bf16
+ *   k/v_cache  : [B, H, Nk, d] bf16        lse : output [B, H, Nq] fp32
+ *   workspace  : device buffer of attn_decode_workspace_bytes(B, H, Nq, Nk, d)
+ *                bytes (partial results; contents on entry ignored)
+ * Supported: dtype ATTN_BF16, d in {64, 128}, 1 <= Nq <= 8, Nk <= 2^23
+ * (ATTN_ERR_UNSUPPORTED otherwise); causal needs Nq <= Nk; B*H*Nk < 2^31.
+ * attn_decode_workspace_bytes returns 0 for arguments attn_decode rejects.
+ * Other conventions as above (caller-owned buffers, enqueue only). */
+size_t attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
+attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
+                          attn_dtype_t dtype, float scale, int causal, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* attn_status_string(attn_status_t s);

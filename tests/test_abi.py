@@ -34,7 +34,8 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess", "attn_bwd_dkdv",
         "attn_bwd_dq", "attn_status_string", "attn_abi_version", "attn_fwd_block_sparse",
-        "attn_bwd_block_sparse", "attn_fwd_dropout", "attn_bwd_dropout"])
+        "attn_bwd_block_sparse", "attn_fwd_dropout", "attn_bwd_dropout", "attn_decode_workspace_bytes",
+        "attn_decode"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -180,6 +181,36 @@ def test_dropout_validation(lib):
     assert bwd_d(p=2.0) == INV
     assert bwd_d(ws_bytes=ws - 1) == INV
     assert bwd_d(dtype=0) == UNS
+
+
+def test_decode_workspace_and_validation(lib):
+    INV, UNS = binding.ATTN_ERR_INVALID, binding.ATTN_ERR_UNSUPPORTED
+    # chunks of 512 keys; per chunk and query: m, l and d floats, rounded up to 256 bytes
+    assert lib.attn_decode_workspace_bytes(2, 3, 1, 1000, 128) == ((2 * 3 * 2 * 1 * 130 * 4 + 255) // 256) * 256
+    assert lib.attn_decode_workspace_bytes(1, 1, 8, 512, 64) == 8 * 66 * 4 + (256 - (8 * 66 * 4) % 256) % 256
+    assert lib.attn_decode_workspace_bytes(1, 1, 9, 512, 64) == 0
+    assert lib.attn_decode_workspace_bytes(1, 1, 1, 0, 64) == 0
+    assert lib.attn_decode_workspace_bytes(1, 1, 1, 100, 96) == 0
+    ws = lib.attn_decode_workspace_bytes(1, 2, 4, 700, 64)
+
+    def dec(ptrs=None, ws_bytes=ws, Nq=4, Nk=700, d=64, dtype=1, scale=0.125, causal=1):
+        p = ptrs or [FAKE] * 6
+        return lib.attn_decode(*p, ws_bytes, 1, 2, Nq, Nk, d, dtype, scale, causal, None)
+
+    for i in range(6):
+        p = [FAKE] * 6
+        p[i] = None
+        assert dec(p) == INV, i
+    assert dec(ws_bytes=ws - 1) == INV
+    assert dec(Nq=0) == INV
+    assert dec(Nk=0) == INV
+    assert dec(Nq=5, Nk=4) == INV  # causal needs Nq <= Nk
+    assert dec(scale=float("inf")) == INV
+    assert dec(causal=3) == INV
+    assert dec(Nq=9) == UNS
+    assert dec(Nk=(1 << 23) + 1) == UNS
+    assert dec(d=80) == UNS
+    assert dec(dtype=0) == UNS
 
 
 def test_binding_checks_block_mask_shape():
