@@ -124,3 +124,25 @@ def sample_rows(count: int, B: int, H: int, N: int, seed: int):
         h, i = divmod(rem, N)
         out.append((b, h, i))
     return out
+
+
+def draw_fp8(B: int, H: int, N: int, d: int, seed: int = 0):
+    """Q, K, V as OCP e4m3 codes (uint8 CPU tensors [B, H, N, d]) with one
+    fp32 scale per tensor.
+
+    The same N(0, 1) fp32 draws as `draw` (order Q, K, V) are divided by
+    amax / 448 (so the largest magnitude maps to the top of the e4m3 range)
+    and rounded by torch's float8_e4m3fn cast.  The value of code x of Q is
+    dq * e4m3(x).  Returns a dict with q8, k8, v8 and dq, dk, dv (floats).
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    shape = (B, H, N, d)
+    out = {}
+    for name in ("q", "k", "v"):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        amax = float(x.abs().max()) if x.numel() else 1.0
+        descale = float(torch.tensor(max(amax, 1e-30) / 448.0, dtype=torch.float32))
+        out[name + "8"] = (x / descale).to(torch.float8_e4m3fn).view(torch.uint8)
+        out["d" + name] = descale
+    return out
