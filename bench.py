@@ -8,13 +8,15 @@ forward alone.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME]
                     [--batch B] [--heads H] [--no-cpu-baseline]
-                    [--block-density P] [--dropout P] [--decode NQ [--decode-nk NK]]
+                    [--block-density P] [--dropout P] [--fp8] [--decode NQ [--decode-nk NK]]
 
 --block-density P times the block-sparse entry points instead, on a seeded
 random mask over 128 x 128 blocks (each block on with probability P, diagonal
 blocks always on), counting only the allowed (query, key) pairs.
 --dropout P times attn_fwd_dropout + attn_bwd_dropout at rate P (every pair is
 still computed, so the FLOP counts are the dense ones).
+--fp8 times attn_fwd_fp8 on the workload's shape (e4m3 Q, K, V; bf16 O), with
+the bf16 forward on the same shape beside it, priced against the fp8 peak.
 --decode NQ times attn_decode: NQ new queries per head against a KV cache of
 --decode-nk keys (B=4, H=32, d=128 unless --batch/--heads say otherwise),
 priced against HBM bandwidth (it reads each cached key and value once).
@@ -48,6 +50,7 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix peak (published)
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak (published)
 HBM_PEAK_GBS = 8000.0
 
@@ -66,6 +69,7 @@ def parse():
                          "(calibrates the HBM byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
     ap.add_argument("--dropout", type=float, default=None, help="time the dropout entry points at this rate")
+    ap.add_argument("--fp8", action="store_true", help="time attn_fwd_fp8 (e4m3 inputs) on the workload's shape")
     ap.add_argument("--decode", type=int, default=None, help="time attn_decode with this many queries per head")
     ap.add_argument("--decode-nk", type=int, default=16384, help="cached keys per head for --decode")
     ap.add_argument("--block-density", type=float, default=None,
@@ -384,6 +388,66 @@ def bench_block_sparse(args, w):
     return 0
 
 
+def bench_fp8(args, w):
+    """The FP8 forward (e4m3 Q, K, V with per-tensor scales, bf16 O) on the
+    workload's shape, with the bf16 forward on the same shape timed beside it;
+    prints one JSON line."""
+    import exact_io_aware_23_amd as A
+
+    dev = torch.device("cuda", 0)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    inp = W.draw_fp8(B, H, N, d, seed=w.seed)
+    q8, k8, v8 = (inp[x].to(dev) for x in ("q8", "k8", "v8"))
+    ref = W.draw(B, H, N, d, "bf16", seed=w.seed, backward=False)
+    qb, kb, vb = (ref[x].to(dev) for x in ("q", "k", "v"))
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e in ev:
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        return wall_ms, sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+
+    ms_step, t_fp8 = timed(lambda: A.fwd_fp8(q8, k8, v8, inp["dq"], inp["dk"], inp["dv"], scale=w.scale,
+                                               causal=w.causal, out=o, lse=lse))
+    _, t_bf16 = timed(lambda: A.fwd(qb, kb, vb, scale=w.scale, causal=w.causal, out=o, lse=lse))
+    F = w.fwd_flops()
+    achieved = F / (t_fp8 * 1e-3) / 1e12
+    out = {
+        "metric": "attention forward TFLOP/s, fp8 e4m3 inputs",
+        "value": round(F / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name + "_fp8", "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "pass": "fwd"},
+        "fwd_tflops": round(achieved, 2),
+        "bf16_fwd_tflops_same_shape": round(F / (t_bf16 * 1e-3) / 1e12, 2),
+        "kernel_ms": {"fwd_fp8": round(t_fp8, 4), "fwd_bf16": round(t_bf16, 4)},
+        "roofline": {"kernel": "fwd_fp8", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(t_fp8, 4)},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -408,6 +472,8 @@ def main():
         return bench_dropout(args, w)
     if args.decode is not None:
         return bench_decode(args)
+    if args.fp8:
+        return bench_fp8(args, w)
     fwd_only = args.which == "fwd" or not w.backward
     dev = torch.device("cuda", 0)
     inp = W.draw_workload(w, B=w.B, H=w.H)

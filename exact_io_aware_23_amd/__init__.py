@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     fwd,
     fwd_block_sparse,
     fwd_dropout,
+    fwd_fp8,
     load_library,
     status_string,
 )

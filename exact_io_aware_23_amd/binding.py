@@ -38,6 +38,7 @@ _SIGNATURES = {
                               _P]),
     "attn_decode_workspace_bytes": (_S, [_I, _I, _I, _I, _I]),
     "attn_decode": (_I, [_P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_fwd_fp8": (_I, [_P, _P, _P, _F, _F, _F, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_abi_version": (_I, []),
 }
@@ -131,6 +132,27 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None =
     _check("lse", lse, (B, H, N), torch.float32)
     _call("attn_fwd", q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
           _dtype_code(q), _default_scale(d, scale), int(bool(causal)), _stream(q.device))
+    return out, lse
+
+
+def fwd_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, descale_q: float, descale_k: float,
+            descale_v: float, scale: float | None = None, causal: bool = False, out=None, lse=None):
+    """attn_fwd_fp8: q8, k8, v8 are e4m3 codes [B, H, N, d] (torch.uint8 or
+    torch.float8_e4m3fn) with one scale per tensor; returns (O bf16, L fp32)."""
+    B, H, N, d = q8.shape
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        if not isinstance(t, torch.Tensor) or t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{name} must be a uint8 or float8_e4m3fn tensor")
+        _check(name, t, (B, H, N, d), t.dtype)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device)
+    _check("out", out, (B, H, N, d), torch.bfloat16)
+    _check("lse", lse, (B, H, N), torch.float32)
+    _call("attn_fwd_fp8", q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), float(descale_q), float(descale_k),
+          float(descale_v), out.data_ptr(), lse.data_ptr(), B, H, N, d, _default_scale(d, scale),
+          int(bool(causal)), _stream(q8.device))
     return out, lse
 
 

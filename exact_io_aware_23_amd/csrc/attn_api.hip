@@ -222,6 +222,20 @@ attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cach
                                      d, scale, causal != 0, (hipStream_t)stream));
 }
 
+attn_status_t attn_fwd_fp8(const void* q, const void* k, const void* v, float descale_q, float descale_k,
+                           float descale_v, void* o, float* lse, int B, int H, int N, int d, float scale,
+                           int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  if (!scale_ok(descale_q) || !scale_ok(descale_k) || !scale_ok(descale_v)) return ATTN_ERR_INVALID;
+  const float c = (float)((double)scale * descale_q * descale_k);
+  if (!scale_ok(c)) return ATTN_ERR_INVALID;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (N > (1 << 22)) return ATTN_ERR_UNSUPPORTED;  // 32-bit byte offsets within a head
+  return map_hip(attn::launch_fwd_fp8(q, k, v, o, lse, B * H, N, d, scale, descale_q, descale_k, descale_v,
+                                      causal != 0, (hipStream_t)stream));
+}
+
 const char* attn_status_string(attn_status_t s) {
   switch (s) {
     case ATTN_OK: return "ok";

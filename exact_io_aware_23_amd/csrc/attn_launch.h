@@ -44,6 +44,10 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const floa
                          int d, float scale, bool causal, const BlockMask& mask, const DropParams& drop,
                          hipStream_t stream);
 
+// FP8 forward: q, k, v are e4m3 codes, o bf16; S = scale dq dk Q K^T, O = dv P V.
+hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
+                          float scale, float dq, float dk, float dv, bool causal, hipStream_t stream);
+
 // Decode against a KV cache: Nq <= decode_max_queries() queries per
 // (batch, head), Nk cached keys, split into decode_chunks(Nk) chunks whose
 // partial results (m, l: BH*S*Nq floats each, then O: BH*S*Nq*d floats) live

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 typedef enum {
   ATTN_OK = 0,
@@ -200,6 +200,30 @@ size_t attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d);
 attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                           void* workspace, size_t workspace_bytes, int B, int H, int Nq, int Nk, int d,
                           attn_dtype_t dtype, float scale, int causal, void* stream);
+
+/* FP8 forward.  "What is Flash Attention?" (iania.ai video page, English),
+ * 09:29: the third generation of the method adds an FP8 forward.  Q, K, V are
+ * OCP OFP8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * S.1111.111 is NaN; largest finite 448; the bytes of torch.float8_e4m3fn)
+ * with one fp32 scale per tensor: the value of code x of Q is descale_q * x.
+ * Computes the attention of the dequantized tensors:
+ *     S = scale * (descale_q Q)(descale_k K)^T,  O = softmax(S + mask) (descale_v V),
+ *     L = logsumexp of each row of S + mask (natural log).
+ * Accuracy: S and l are formed in fp32 from exact fp8 products; P is rounded
+ * to e4m3 (nearest even, in units of a reference max within 2^8 of the row
+ * max) before the product with V, so each O element carries an error of at
+ * most [2^-4 sum_j p_j |v_j| + 2^-10 sum_{p_j < 2^-6} |v_j|] / sum_j p_j
+ * (p_j = e^(S_j - max S) of its row) plus the bf16 rounding of O.
+ *   q, k, v : [B, H, N, d] uint8 e4m3 codes, 16-byte aligned; NaN codes give NaN.
+ *   descale_q, descale_k, descale_v : finite and > 0; scale * descale_q *
+ *             descale_k must be a finite positive fp32 value.
+ *   o   : output [B, H, N, d] bf16 (round to nearest even).
+ *   lse : output [B, H, N] fp32.
+ * Supported: d in {64, 128}, N <= 2^22 (ATTN_ERR_UNSUPPORTED otherwise);
+ * causal as for attn_fwd.  Other conventions as above. */
+attn_status_t attn_fwd_fp8(const void* q, const void* k, const void* v, float descale_q, float descale_k,
+                           float descale_v, void* o, float* lse, int B, int H, int N, int d, float scale,
+                           int causal, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* attn_status_string(attn_status_t s);

@@ -91,8 +91,9 @@ def attention_forward_fp8(q8, k8, v8, dq: float, dk: float, dv: float, scale: fl
 _U = 1.0 / np.sqrt(12.0)
 
 
-def _error_model(p_t: np.ndarray, v: np.ndarray):
-    """Bound and scale of the O error caused by rounding P to e4m3.
+def _error_model(p_t: np.ndarray, v: np.ndarray, eps=None):
+    """Bound and scale of the O error caused by rounding P to e4m3, and by
+    score errors of at most eps per row (eps [r, 1]; None = exact scores).
 
     p_t [r, n]: row-normalised probabilities e^(S - max S) (masked = 0),
     v [n, d]: dequantized V.  A kernel rounds p = sigma p_t with 1 <= sigma
@@ -103,8 +104,13 @@ def _error_model(p_t: np.ndarray, v: np.ndarray):
 
         |dO| <= [2^-4 sum p_t |v| + 2^-10 sum_{p_t < 2^-6} |v|] / l_t,
 
-    and p < 2^-6 implies p_t < 2^-6 since sigma >= 1.  The error scale
-    treats each rounding error as spread evenly over its quantum
+    and p < 2^-6 implies p_t < 2^-6 since sigma >= 1.  Scores off by at
+    most eps scale each p by a factor in [e^-eps, e^eps]: the rounding term
+    grows by at most e^(2 eps) and the weights of the convex combination
+    O = sum p v / sum p move by at most (e^(2 eps) - 1) sum p_t |v| / l_t;
+    L moves by at most eps (logsumexp is 1-Lipschitz in the max norm).  The
+    error scale covers the P rounding only.  It
+treats each rounding error as spread evenly over its quantum
     (sigma_abs = quantum / sqrt 12), with the largest relative quantum of a
     binade (2^-3 p) and sigma = 1 for the subnormals, so it tends to
     overstate the error.
@@ -112,25 +118,43 @@ def _error_model(p_t: np.ndarray, v: np.ndarray):
     l_t = p_t.sum(axis=1, keepdims=True)
     av = np.abs(v)
     tiny = ((p_t < E4M3_MIN_NORMAL) & (p_t > 0)).astype(np.float64)
-    bound = (2.0 ** -4 * (p_t @ av) + 2.0 ** -10 * (tiny @ av)) / l_t
+    pv = (p_t @ av) / l_t
+    bound = 2.0 ** -4 * pv + 2.0 ** -10 * (tiny @ av) / l_t
+    if eps is not None:
+        grow = np.expm1(2.0 * np.asarray(eps, dtype=np.float64).reshape(-1, 1))
+        bound = (1.0 + grow) * bound + grow * pv
     var = (2.0 ** -3 * _U) ** 2 * ((p_t * p_t) @ (v * v)) + (E4M3_SUBNORMAL_STEP * _U) ** 2 * (tiny @ (v * v))
     return bound, np.sqrt(var) / l_t
 
 
-def error_model_head(q8, k8, v8, dq: float, dk: float, dv: float, scale: float, causal: bool):
-    """(bound, sigma) [n, d] of one head's O for P rounded to e4m3 (see _error_model)."""
+def _score_eps(q, k, scale: float, allowed, s_rel: float):
+    """Per-row bound s_rel * max over allowed keys of scale * sum_k |q_k k_k|:
+    the error of scores formed by a contraction whose rounding error is at
+    most s_rel times the sum of the magnitudes of its products."""
+    mag = scale * (np.abs(q) @ np.abs(k).T)
+    mag = np.where(allowed, mag, 0.0)
+    return s_rel * mag.max(axis=1, keepdims=True)
+
+
+def error_model_head(q8, k8, v8, dq: float, dk: float, dv: float, scale: float, causal: bool,
+                     s_rel: float = 0.0):
+    """(bound [n, d], sigma [n, d], eps [n]) for one head's O and L with P
+    rounded to e4m3 and scores formed with relative precision s_rel (of the
+    sum of product magnitudes); see _error_model.  |L - L_ref| <= eps."""
     q, k, v = dequantize(q8, dq), dequantize(k8, dk), dequantize(v8, dv)
     s = orc.scores_head(q, k, scale, causal)
     m = np.max(s, axis=1, keepdims=True)
     p_t = np.where(np.isfinite(s), np.exp(s - m), 0.0)
-    return _error_model(p_t, v)
+    eps = _score_eps(q, k, scale, np.isfinite(s), s_rel)
+    bound, sigma = _error_model(p_t, v, eps)
+    return bound, sigma, eps[:, 0]
 
 
 def forward_rows_fp8(q8_rows, rows: Sequence[int], k8, v8, dq: float, dk: float, dv: float, scale: float,
-                     causal: bool):
-    """O, L, bound and sigma for the listed query rows of one head: q8_rows
-    [r, d] holds the codes of rows `rows` (their positions, for the causal
-    mask); k8, v8 are the head's [n, d] codes."""
+                     causal: bool, s_rel: float = 0.0):
+    """O, L, bound, sigma and eps for the listed query rows of one head:
+    q8_rows [r, d] holds the codes of rows `rows` (their positions, for the
+    causal mask); k8, v8 are the head's [n, d] codes."""
     q = dequantize(q8_rows, dq)
     k, v = dequantize(k8, dk), dequantize(v8, dv)
     o, lse = orc.forward_rows(q, rows, k, v, scale, causal)
@@ -140,5 +164,6 @@ def forward_rows_fp8(q8_rows, rows: Sequence[int], k8, v8, dq: float, dk: float,
         s = np.where(np.arange(n)[None, :] <= np.asarray(rows)[:, None], s, -np.inf)
     m = np.max(s, axis=1, keepdims=True)
     p_t = np.where(np.isfinite(s), np.exp(s - m), 0.0)
-    bound, sigma = _error_model(p_t, v)
-    return o, lse, bound, sigma
+    eps = _score_eps(q, k, scale, np.isfinite(s), s_rel)
+    bound, sigma = _error_model(p_t, v, eps)
+    return o, lse, bound, sigma, eps[:, 0]

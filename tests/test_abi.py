@@ -35,7 +35,7 @@ def test_header_declares_the_expected_entry_points():
         "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess", "attn_bwd_dkdv",
         "attn_bwd_dq", "attn_status_string", "attn_abi_version", "attn_fwd_block_sparse",
         "attn_bwd_block_sparse", "attn_fwd_dropout", "attn_bwd_dropout", "attn_decode_workspace_bytes",
-        "attn_decode"])
+        "attn_decode", "attn_fwd_fp8"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -211,6 +211,26 @@ def test_decode_workspace_and_validation(lib):
     assert dec(Nk=(1 << 23) + 1) == UNS
     assert dec(d=80) == UNS
     assert dec(dtype=0) == UNS
+
+
+def test_fp8_validation(lib):
+    INV, UNS = binding.ATTN_ERR_INVALID, binding.ATTN_ERR_UNSUPPORTED
+
+    def f8(ptrs=None, dq=0.01, dk=0.01, dv=0.01, N=300, d=128, scale=0.088, causal=1):
+        p = ptrs or [FAKE] * 5
+        return lib.attn_fwd_fp8(p[0], p[1], p[2], dq, dk, dv, p[3], p[4], 1, 2, N, d, scale, causal, None)
+
+    for i in range(5):
+        p = [FAKE] * 5
+        p[i] = None
+        assert f8(p) == INV, i
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert f8(dq=bad) == INV and f8(dk=bad) == INV and f8(dv=bad) == INV and f8(scale=bad) == INV
+    assert f8(dq=1e-30, dk=1e-30) == INV  # scale dq dk underflows fp32
+    assert f8(N=0) == INV
+    assert f8(causal=2) == INV
+    assert f8(d=96) == UNS
+    assert f8(N=(1 << 22) + 1) == UNS
 
 
 def test_binding_checks_block_mask_shape():

@@ -155,7 +155,7 @@ def test_error_model_against_emulation(causal, sigma_mode):
     ls = {"one": np.zeros((n, n_tiles)), "max": np.full((n, n_tiles), 8.0),
           "random": r.uniform(0, 8, (n, n_tiles))}[sigma_mode]
     o, _ = fp8.forward_head_fp8(*args)
-    bound, sigma = fp8.error_model_head(*args)
+    bound, sigma, _ = fp8.error_model_head(*args)
     err = np.abs(emulate(*args, ls) - o)
     assert np.all(err <= bound)
     z = np.sqrt(np.mean((err / sigma) ** 2))
@@ -181,10 +181,37 @@ def test_rows_match_head():
     q8, k8, v8 = (random_codes(r, (n, d)) for _ in range(3))
     args = (0.01, 0.01, 0.1, 0.2, True)
     o, lse = fp8.forward_head_fp8(q8, k8, v8, *args)
-    bound, sigma = fp8.error_model_head(q8, k8, v8, *args)
+    bound, sigma, eps = fp8.error_model_head(q8, k8, v8, *args, s_rel=2.0 ** -13)
     rows = [0, 7, 64, 149]
-    o_r, l_r, b_r, s_r = fp8.forward_rows_fp8(q8[rows], rows, k8, v8, *args)
+    o_r, l_r, b_r, s_r, e_r = fp8.forward_rows_fp8(q8[rows], rows, k8, v8, *args, s_rel=2.0 ** -13)
     np.testing.assert_allclose(o_r, o[rows], rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(l_r, lse[rows], rtol=1e-13)
     np.testing.assert_allclose(b_r, bound[rows], rtol=1e-12)
     np.testing.assert_allclose(s_r, sigma[rows], rtol=1e-12)
+    np.testing.assert_allclose(e_r, eps[rows], rtol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_score_error_terms_against_perturbation(seed):
+    """Scores perturbed by at most eps (here the eps of a contraction with
+    relative precision 2^-10 of the product magnitudes, chosen at its extreme
+    +-eps per entry): L moves by at most eps and O by at most the bound's
+    score term (no P rounding in this check: the perturbed result is exact)."""
+    r = np.random.default_rng(20 + seed)
+    n, d = 120, 16
+    q8, k8, v8 = (random_codes(r, (n, d)) for _ in range(3))
+    args = (0.01, 0.02, 0.1, 0.3, bool(seed % 2))
+    o, lse = fp8.forward_head_fp8(q8, k8, v8, *args)
+    b0, _, _ = fp8.error_model_head(q8, k8, v8, *args, s_rel=0.0)
+    b1, _, eps = fp8.error_model_head(q8, k8, v8, *args, s_rel=2.0 ** -10)
+    assert np.all(eps > 0)
+    q, k, v = fp8.dequantize(q8, 0.01), fp8.dequantize(k8, 0.02), fp8.dequantize(v8, 0.1)
+    s = orc.scores_head(q, k, 0.3, args[-1])
+    s2 = s + eps[:, None] * r.choice([-1.0, 1.0], s.shape)
+    p, m, l = orc._safe_softmax(s2)
+    o2 = p @ v
+    lse2 = m + np.log(l)
+    assert np.all(np.abs(lse2 - lse) <= eps * (1 + 1e-12))
+    # the score part of the bound: b1 - e^(2 eps) b0 = (e^(2 eps) - 1) sum p_t |v| / l_t
+    score_term = b1 - np.exp(2 * eps)[:, None] * b0
+    assert np.all(np.abs(o2 - o) <= score_term * (1 + 1e-9) + 1e-15)
