@@ -404,8 +404,10 @@ def bench_fp8(args, w):
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    warm = max(args.warmup, 50)  # one launch is under a millisecond: give the clocks ~40 ms to settle
+
     def timed(fn):
-        for _ in range(args.warmup):
+        for _ in range(warm):
             fn()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         torch.cuda.synchronize()
@@ -436,7 +438,8 @@ def bench_fp8(args, w):
         "vs_baseline": None,
         "dtype": "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": w.name + "_fp8", "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "pass": "fwd"},
+        "config": {"workload": w.name + "_fp8", "B": B, "H": H, "N": N, "d": d, "causal": w.causal, "pass": "fwd",
+                   "warmup_launches": warm},
         "fwd_tflops": round(achieved, 2),
         "bf16_fwd_tflops_same_shape": round(F / (t_bf16 * 1e-3) / 1e12, 2),
         "kernel_ms": {"fwd_fp8": round(t_fp8, 4), "fwd_bf16": round(t_bf16, 4)},

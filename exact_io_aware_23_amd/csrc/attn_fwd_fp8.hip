@@ -28,6 +28,8 @@
 //     K/V tiles double-buffered in LDS through buffer -> LDS copies, one
 //     barrier per tile, scores of tile j+1 interleaved with tile j's
 //     exponentials and P V, causal tile skipping, XCD-aware work order.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -239,10 +241,13 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
         rs += p;
       }
     l_run += rs;
+    // (the first conversion of a word writes its low half and keeps the high
+    // half of its third operand, which the second overwrites: passing a
+    // register that dies there instead of 0 saves a v_mov per word)
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int kb = w >> 2, r = 4 * (w & 3);
-      int x = __builtin_amdgcn_cvt_pk_fp8_f32(st[kb][r], st[kb][r + 1], 0, false);
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(st[kb][r], st[kb][r + 1], __builtin_bit_cast(int, st[kb][r]), false);
       x = __builtin_amdgcn_cvt_pk_fp8_f32(st[kb][r + 2], st[kb][r + 3], x, true);
       pop[w] = x;
     }
@@ -295,11 +300,18 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
   }
   __syncthreads();  // every wave has read K(0) before K(2) is loaded over it
 
-  auto step = [&](int j, int par, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+  // A step whose next tile needs no mask (MASKED = false) has no branch
+  // between its MFMAs and the next tile's max, so the row sums and the max
+  // stay in the instruction stream of the MFMAs instead of being moved past
+  // a join.  Tiles 0 .. jm-1 of this wave need no mask.
+  const int lim = CAUSAL ? min(N, q0w + 1) : N;
+  const int jm = uniform(max(lim, 0) / C::BC);
+  auto step = [&](int j, int par, f32x16 (&cur)[2], f32x16 (&nxt)[2], auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int kv_a = (j + 1) * C::BC;
     if (j + 2 < n_tiles) load_k((j + 2) * C::BC, par);
     if (j + 1 < n_tiles) load_v(kv_a, par ^ 1);
-    if (j < wave_tiles) {
+    if (!MASKED || j < wave_tiles) {
       // the scores of tile j+1 are formed even when this wave has no such
       // tile (the slot holds an in-bounds K tile whose keys the mask removes)
       i32x8 pop;
@@ -308,18 +320,28 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
       pv(par, pop);
       pin_a();
       pin_b();
-      if (needs_mask(kv_a)) mask(nxt, kv_a);
-      if (j + 1 < wave_tiles) rescale(tile_max(nxt));
+      if constexpr (MASKED) {
+        if (needs_mask(kv_a)) mask(nxt, kv_a);
+        if (j + 1 < wave_tiles) rescale(tile_max(nxt));
+      } else {
+        rescale(tile_max(nxt));
+      }
     }
     wait_vmem_all();
     __syncthreads();
   };
+  using Plain = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
   int j = 0;
-  for (; j + 1 < n_tiles; j += 2) {
-    step(j, 0, sa, sb);
-    step(j + 1, 1, sb, sa);
+  for (; j + 2 < jm; j += 2) {  // tiles j+1 and j+2 need no mask
+    step(j, 0, sa, sb, Plain{});
+    step(j + 1, 1, sb, sa, Plain{});
   }
-  if (j < n_tiles) step(j, 0, sa, sb);
+  for (; j + 1 < n_tiles; j += 2) {
+    step(j, 0, sa, sb, Masked{});
+    step(j + 1, 1, sb, sa, Masked{});
+  }
+  if (j < n_tiles) step(j, 0, sa, sb, Masked{});
 
   // ---- epilogue: O = dv O_acc / l, L = (m + log2 l) ln 2
   const float lt = pair_sum(l_run);
