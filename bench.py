@@ -153,7 +153,8 @@ def kernel_source_hash(kernel: str) -> str:
     """sha256 of the HIP source file that holds `kernel` (its code plus the shared header)."""
     import hashlib
 
-    src = {"fwd": "attn_fwd.hip", "preprocess": "attn_bwd.hip", "dq": "attn_bwd.hip", "dkdv": "attn_bwd.hip"}[kernel]
+    src = {"fwd": "attn_fwd.hip", "preprocess": "attn_bwd.hip", "dq": "attn_bwd.hip", "dkdv": "attn_bwd.hip",
+           "fwd_fp8": "attn_fwd_fp8.hip"}[kernel]
     h = hashlib.sha256()
     for f in (src, "attn_common.h"):
         with open(os.path.join(ROOT, "exact_io_aware_23_amd", "csrc", f), "rb") as fh:
@@ -445,7 +446,8 @@ def bench_fp8(args, w):
         "kernel_ms": {"fwd_fp8": round(t_fp8, 4), "fwd_bf16": round(t_bf16, 4)},
         "roofline": {"kernel": "fwd_fp8", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_FP8_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
-                     "traffic": None, "avg_launch_ms": round(t_fp8, 4)},
+                     "traffic": measured_traffic("fwd_fp8", w.name + "_fp8") if (B, H) == (2, 32) else None,
+                     "avg_launch_ms": round(t_fp8, 4)},
     }
     print(json.dumps(out), flush=True)
     return 0
