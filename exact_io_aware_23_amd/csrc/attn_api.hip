@@ -17,6 +17,9 @@ bool sizes_ok(int B, int H, int N) {
 
 bool scale_ok(float scale) { return std::isfinite(scale) && scale > 0.f; }
 
+// the kernels address one (batch, head) slab with 32-bit byte offsets
+constexpr int kMaxN = 1 << 22;
+
 attn_status_t map_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
 attn_status_t check_bf16_d(int d, attn_dtype_t dtype) {
@@ -34,6 +37,7 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, flo
                        int N, int d, attn_dtype_t dtype, float scale, int causal, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID;
   if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
   if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   return map_hip(attn::launch_fwd(q, k, v, o, lse, B * H, N, d, dtype == ATTN_BF16, scale, causal != 0,
@@ -57,6 +61,7 @@ attn_status_t attn_bwd_preprocess(const void* o, const void* dout, float* delta,
                                   attn_dtype_t dtype, void* stream) {
   if (!o || !dout || !delta) return ATTN_ERR_INVALID;
   if (!sizes_ok(B, H, N)) return ATTN_ERR_INVALID;
+  if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
   const attn_status_t s = check_bf16_d(d, dtype);
   if (s != ATTN_OK) return s;
   return map_hip(attn::launch_bwd_preprocess(o, dout, delta, B * H, N, d, (hipStream_t)stream));
@@ -67,6 +72,7 @@ attn_status_t attn_bwd_dkdv(const void* q, const void* k, const void* v, const f
                             attn_dtype_t dtype, float scale, int causal, void* stream) {
   if (!q || !k || !v || !lse || !dout || !delta || !dk || !dv) return ATTN_ERR_INVALID;
   if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
   const attn_status_t s = check_bf16_d(d, dtype);
   if (s != ATTN_OK) return s;
   return map_hip(attn::launch_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, B * H, N, d, scale, causal != 0,
@@ -78,6 +84,7 @@ attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const flo
                           attn_dtype_t dtype, float scale, int causal, void* stream) {
   if (!q || !k || !v || !lse || !dout || !delta || !dq || !delta_out) return ATTN_ERR_INVALID;
   if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
   const attn_status_t s = check_bf16_d(d, dtype);
   if (s != ATTN_OK) return s;
   return map_hip(attn::launch_bwd_dq(q, k, v, lse, dout, delta, dq, delta_out, B * H, N, d, scale,
@@ -137,6 +144,7 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        int causal, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID;
   if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
   const attn_status_t s = check_bf16_d(d, dtype);
   if (s != ATTN_OK) return s;
   if (workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d)) return ATTN_ERR_INVALID;
@@ -149,6 +157,7 @@ attn_status_t attn_fwd_block_sparse(const void* q, const void* k, const void* v,
                                     attn_dtype_t dtype, float scale, int causal, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID;
   if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
   attn_status_t s = check_mask(block_mask, mask_heads, B, H, N);
   if (s == ATTN_OK) s = check_bf16_d(d, dtype);
   if (s != ATTN_OK) return s;
@@ -163,6 +172,7 @@ attn_status_t attn_bwd_block_sparse(const void* q, const void* k, const void* v,
                                     float scale, int causal, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID;
   if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
   attn_status_t s = check_mask(block_mask, mask_heads, B, H, N);
   if (s == ATTN_OK) s = check_bf16_d(d, dtype);
   if (s != ATTN_OK) return s;
@@ -176,6 +186,7 @@ attn_status_t attn_fwd_dropout(const void* q, const void* k, const void* v, void
                                int causal, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID;
   if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
   attn::DropParams dr;
   attn_status_t s = make_drop(p_drop, seed, &dr);
   if (s == ATTN_OK) s = check_bf16_d(d, dtype);
@@ -190,6 +201,7 @@ attn_status_t attn_bwd_dropout(const void* q, const void* k, const void* v, cons
                                attn_dtype_t dtype, float scale, int causal, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID;
   if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
   attn::DropParams dr;
   attn_status_t s = make_drop(p_drop, seed, &dr);
   if (s == ATTN_OK) s = check_bf16_d(d, dtype);
@@ -231,7 +243,7 @@ attn_status_t attn_fwd_fp8(const void* q, const void* k, const void* v, float de
   const float c = (float)((double)scale * descale_q * descale_k);
   if (!scale_ok(c)) return ATTN_ERR_INVALID;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  if (N > (1 << 22)) return ATTN_ERR_UNSUPPORTED;  // 32-bit byte offsets within a head
+  if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
   return map_hip(attn::launch_fwd_fp8(q, k, v, o, lse, B * H, N, d, scale, descale_q, descale_k, descale_v,
                                       causal != 0, (hipStream_t)stream));
 }

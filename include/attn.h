@@ -33,7 +33,9 @@
  *     fault shows up at the caller's next synchronisation.
  *   - Supported: dtype ATTN_BF16 with d in {64, 128} for every entry point;
  *     dtype ATTN_F32 with d in {64, 128} for attn_fwd only.  N >= 1 (any N,
- *     not only multiples of the tile size), B, H >= 1, B*H*N < 2^31.
+ *     not only multiples of the tile size), B, H >= 1, B*H*N < 2^31
+ *     (ATTN_ERR_INVALID otherwise), and N <= 2^22 (ATTN_ERR_UNSUPPORTED
+ *     otherwise: one head is addressed with 32-bit byte offsets).
  */
 #ifndef EXACT_ATTN_H
 #define EXACT_ATTN_H

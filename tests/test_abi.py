@@ -85,6 +85,7 @@ def test_fwd_validation(lib):
     assert fwd(lib, d=96) == UNS
     assert fwd(lib, d=256) == UNS
     assert fwd(lib, dtype=7) == UNS
+    assert fwd(lib, N=(1 << 22) + 1) == UNS  # one head is addressed with 32-bit byte offsets
 
 
 def test_bwd_validation(lib):
@@ -105,6 +106,10 @@ def test_bwd_validation(lib):
     assert bwd(causal=-1) == INV
     assert bwd(d=32) == UNS
     assert bwd(dtype=0) == UNS  # fp32 backward is not provided
+    assert bwd(N=(1 << 22) + 1) == UNS
+    assert lib.attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 1, (1 << 22) + 1, 64, 1, None) == UNS
+    assert lib.attn_bwd_dkdv(*([FAKE] * 8), 1, 1, (1 << 22) + 1, 64, 1, 0.1, 0, None) == UNS
+    assert lib.attn_bwd_dq(*([FAKE] * 8), 1, 1, (1 << 22) + 1, 64, 1, 0.1, 0, None) == UNS
     assert lib.attn_bwd_preprocess(FAKE, FAKE, None, 1, 1, 8, 64, 1, None) == INV
     assert lib.attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 1, 8, 80, 1, None) == UNS
     assert lib.attn_bwd_dkdv(*([FAKE] * 7), None, 1, 1, 8, 64, 1, 0.1, 0, None) == INV
