@@ -22,6 +22,8 @@
 //     l = sum 2^(m_c - m) l_c, O = sum 2^(m_c - m) O_c / l.
 // Scores are kept in base-2 units (scale * log2 e folded in), as in the
 // forward kernel.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -32,7 +34,9 @@ constexpr int kDecChunk = 512;  // keys per workgroup
 constexpr int kDecTile = 64;    // keys per pass-1 tile (4 threads per key)
 constexpr int kDecMaxQ = 8;     // most queries per call
 
-template <int D>
+// NQ: query capacity of the instantiation (1, 2, 4 or 8 >= nq); registers and
+// LDS scale with it, so a one-query call keeps more workgroups per CU in flight
+template <int D, int NQ>
 __global__ void __launch_bounds__(256)
 decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                       float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, int Nk, int nq,
@@ -40,9 +44,10 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
   constexpr int DP = D / 4;          // dims per thread in pass 1
   constexpr int G8 = D / 8;          // 8-dim groups in pass 2
   constexpr int KL = 256 / G8;       // key lanes in pass 2
-  __shared__ __attribute__((aligned(16))) float qs[kDecMaxQ][D];
-  __shared__ float sc[kDecMaxQ][kDecChunk];
-  __shared__ __attribute__((aligned(16))) float red[4][kDecMaxQ][D];
+  static_assert(NQ >= 1 && NQ <= kDecMaxQ, "query capacity");
+  __shared__ __attribute__((aligned(16))) float qs[NQ][D];
+  __shared__ float sc[NQ][kDecChunk];
+  __shared__ __attribute__((aligned(16))) float red[4][NQ][D];
 
   const int bh = blockIdx.x / S;
   const int s = blockIdx.x % S;
@@ -72,7 +77,7 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
         for (int e = 0; e < 8; ++e) kv[8 * i + e] = (float)b[e];
       }
 #pragma unroll
-      for (int qi = 0; qi < kDecMaxQ; ++qi) {
+      for (int qi = 0; qi < NQ; ++qi) {
         if (qi >= nq) break;
         float acc = 0.f;
 #pragma unroll
@@ -115,9 +120,9 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
 
   // ---- pass 2: unnormalised O_c = sum_j p_j V_j over the chunk
   const int g8 = tid % G8, kl2 = tid / G8;
-  float acc[kDecMaxQ][8];
+  float acc[NQ][8];
 #pragma unroll
-  for (int qi = 0; qi < kDecMaxQ; ++qi)
+  for (int qi = 0; qi < NQ; ++qi)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[qi][e] = 0.f;
 #pragma unroll 4
@@ -127,7 +132,7 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
 #pragma unroll
     for (int e = 0; e < 8; ++e) vv[e] = (float)b[e];
 #pragma unroll
-    for (int qi = 0; qi < kDecMaxQ; ++qi) {
+    for (int qi = 0; qi < NQ; ++qi) {
       if (qi >= nq) break;
       const float p = sc[qi][kj];
 #pragma unroll
@@ -136,7 +141,7 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
   }
   // lanes of one wave with the same g8 hold different keys: fold them
 #pragma unroll
-  for (int qi = 0; qi < kDecMaxQ; ++qi) {
+  for (int qi = 0; qi < NQ; ++qi) {
     if (qi >= nq) break;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -148,7 +153,7 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
   }
   if (lane < G8) {
 #pragma unroll
-    for (int qi = 0; qi < kDecMaxQ; ++qi) {
+    for (int qi = 0; qi < NQ; ++qi) {
       if (qi >= nq) break;
 #pragma unroll
       for (int e = 0; e < 8; ++e) red[wave][qi][8 * g8 + e] = acc[qi][e];
@@ -166,17 +171,31 @@ template <int D>
 __global__ void __launch_bounds__(D)
 decode_merge_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l, const float* __restrict__ ws_o,
                     bf16* __restrict__ O, float* __restrict__ L, int nq, int S) {
+  constexpr int NW = D / 64;
+  __shared__ float wmax[NW];
   const int bh = blockIdx.x / nq, qi = blockIdx.x % nq;
   const int dd = threadIdx.x;
+  const size_t base = (size_t)bh * S * nq + qi;  // partial s of this query sits at base + s * nq
+  // the reference max over the chunks: the threads share the chunks, then
+  // the waves combine their maxima through LDS (all loads independent)
   float m = -INFINITY;
-  for (int s = 0; s < S; ++s) m = fmaxf(m, ws_m[((size_t)bh * S + s) * nq + qi]);
+  for (int s = dd; s < S; s += D) m = fmaxf(m, ws_m[base + (size_t)s * nq]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((dd & 63) == 0) wmax[dd >> 6] = m;
+  __syncthreads();
+  m = wmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) m = fmaxf(m, wmax[w]);
   float l = 0.f, o = 0.f;
   if (m != -INFINITY) {
+    // each thread sums its d column; the chunks' loads do not depend on each
+    // other, so unrolling keeps several in flight
+#pragma unroll 8
     for (int s = 0; s < S; ++s) {
-      const size_t p = ((size_t)bh * S + s) * nq + qi;
+      const size_t p = base + (size_t)s * nq;
       const float ms = ws_m[p];
-      if (ms == -INFINITY) continue;
-      const float a = fast_exp2(ms - m);
+      const float a = ms == -INFINITY ? 0.f : fast_exp2(ms - m);
       l = fmaf(a, ws_l[p], l);
       o = fmaf(a, ws_o[p * D + dd], o);
     }
@@ -199,17 +218,21 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, f
   float* ws_l = ws + parts;
   float* ws_o = ws + 2 * parts;
   const float c = scale * kLog2e;
-  if (d == 64) {
-    hipLaunchKernelGGL((decode_partial_kernel<64>), dim3(BH * S), dim3(256), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, ws_m, ws_l, ws_o, Nk, Nq, S, c, (int)causal);
-    hipLaunchKernelGGL((decode_merge_kernel<64>), dim3(BH * Nq), dim3(64), 0, stream, ws_m, ws_l, ws_o, (bf16*)o,
-                       lse, Nq, S);
-  } else {
-    hipLaunchKernelGGL((decode_partial_kernel<128>), dim3(BH * S), dim3(256), 0, stream, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, ws_m, ws_l, ws_o, Nk, Nq, S, c, (int)causal);
-    hipLaunchKernelGGL((decode_merge_kernel<128>), dim3(BH * Nq), dim3(128), 0, stream, ws_m, ws_l, ws_o,
-                       (bf16*)o, lse, Nq, S);
-  }
+  auto partial = [&](auto dq) {
+    constexpr int D = decltype(dq)::value;
+    auto go = [&](auto nqc) {
+      hipLaunchKernelGGL((decode_partial_kernel<D, decltype(nqc)::value>), dim3(BH * S), dim3(256), 0, stream,
+                         (const bf16*)q, (const bf16*)k, (const bf16*)v, ws_m, ws_l, ws_o, Nk, Nq, S, c, (int)causal);
+    };
+    if (Nq == 1) go(std::integral_constant<int, 1>{});
+    else if (Nq <= 2) go(std::integral_constant<int, 2>{});
+    else if (Nq <= 4) go(std::integral_constant<int, 4>{});
+    else go(std::integral_constant<int, kDecMaxQ>{});
+    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(BH * Nq), dim3(D), 0, stream, ws_m, ws_l, ws_o, (bf16*)o, lse,
+                       Nq, S);
+  };
+  if (d == 64) partial(std::integral_constant<int, 64>{});
+  else partial(std::integral_constant<int, 128>{});
   return hipGetLastError();
 }
 
