@@ -90,37 +90,47 @@ def kernel_flops(w: W.Workload):
     return {"fwd": 2 * one, "dkdv": 4 * one, "dq": 1 * one, "preprocess": 0.0}
 
 
-def cpu_baseline(w: W.Workload, budget_s: float):
-    """Time the fp64 oracle (forward + backward) head by head for about budget_s."""
-    import numpy as np
-    from oracle import attention as orc
+def timed_oracle(run_head, per_head: float, unit: str, budget_s: float, what: str):
+    """Call run_head() (one head of the oracle) until about budget_s has passed.
 
+    per_head is the head's share of the metric's numerator (FLOPs or bytes),
+    so the rate is in the same unit as the GPU line.  cores = the BLAS
+    threads numpy uses.
+    """
     try:
         from threadpoolctl import threadpool_info
 
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    inp = W.draw(1, 1, w.N, w.d, w.dtype, seed=w.seed + 77)
-    q, k, v, do = (inp[x][0, 0].float().numpy().astype(np.float64) for x in ("q", "k", "v", "do"))
     heads = 0
     t0 = time.perf_counter()
     while True:
-        orc.forward_head(q, k, v, w.scale, w.causal)
-        orc.backward_head(q, k, v, do, w.scale, w.causal)
+        run_head()
         heads += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    per_head = (w.fwd_flops() + w.bwd_flops()) / (w.B * w.H)
-    return {
-        "value": per_head * heads / dt / 1e12,
-        "unit": "TFLOP/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": f"{heads} head(s) of the workload (N={w.N}, d={w.d}, causal={w.causal}), forward + backward "
-                  f"in fp64 with S and P materialised, {dt:.1f} s; rate counts the same algorithmic FLOPs as value",
-    }
+    div = 1e12 if unit == "TFLOP/s" else 1e9
+    return {"value": per_head * heads / dt / div, "unit": unit, "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} head(s): {what}, {dt:.1f} s; the rate counts the same algorithmic work as value"}
+
+
+def cpu_baseline(w: W.Workload, budget_s: float):
+    """Time the fp64 oracle (forward + backward) head by head for about budget_s."""
+    import numpy as np
+    from oracle import attention as orc
+
+    inp = W.draw(1, 1, w.N, w.d, w.dtype, seed=w.seed + 77)
+    q, k, v, do = (inp[x][0, 0].float().numpy().astype(np.float64) for x in ("q", "k", "v", "do"))
+
+    def head():
+        orc.forward_head(q, k, v, w.scale, w.causal)
+        orc.backward_head(q, k, v, do, w.scale, w.causal)
+
+    return timed_oracle(head, (w.fwd_flops() + w.bwd_flops()) / (w.B * w.H), "TFLOP/s", budget_s,
+                        f"the workload (N={w.N}, d={w.d}, causal={w.causal}), forward + backward in fp64 with S "
+                        "and P materialised")
 
 
 COPY_BYTES = 1 << 30
@@ -247,6 +257,13 @@ def bench_decode(args):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "avg_launch_ms": round(t_gpu, 4)},
     }
+    if not args.no_cpu_baseline:
+        from oracle import decode as dec
+
+        qh, kh, vh = (t[0, 0].double().numpy() for t in (W.draw(B, H, Nq, d, "bf16", seed=6001, backward=False)["q"],
+                                                         cache["k"], cache["v"]))
+        out["cpu_baseline"] = timed_oracle(lambda: dec.decode_head(qh, kh, vh, scale, True), bytes_ / (B * H), "GB/s",
+                                           args.cpu_seconds, f"decode of head (0, 0), Nq={Nq} Nk={Nk} d={d}, fp64")
     print(json.dumps(out), flush=True)
     return 0
 
@@ -312,6 +329,19 @@ def bench_dropout(args, w):
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "avg_launch_ms": round(t_fwd, 4)},
     }
+    if not args.no_cpu_baseline:
+        from oracle import dropout as drp
+
+        qh, kh, vh, doh = (inp[x][0, 0].double().numpy() for x in ("q", "k", "v", "do"))
+        t = drp.threshold(args.dropout)
+
+        def head():
+            drp.forward_head_dropout(qh, kh, vh, w.scale, w.causal, seed, t, 0)
+            drp.backward_head_dropout(qh, kh, vh, doh, w.scale, w.causal, seed, t, 0)
+
+        out["cpu_baseline"] = timed_oracle(head, (F_fwd + F_bwd) / (B * H), "TFLOP/s", args.cpu_seconds,
+                                           f"head (0, 0), N={N} d={d}, forward + backward with dropout {args.dropout} "
+                                           "in fp64 (Philox decisions regenerated in numpy)")
     print(json.dumps(out), flush=True)
     return 0
 
@@ -385,6 +415,20 @@ def bench_block_sparse(args, w):
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "avg_launch_ms": round(t_fwd, 4)},
     }
+    if not args.no_cpu_baseline:
+        from oracle import attention as orc
+
+        qh, kh, vh, doh = (inp[x][0, 0].double().numpy() for x in ("q", "k", "v", "do"))
+        mh = mask[0].numpy()
+        pairs0 = int(allowed_pairs_per_head(mask[:1], N, w.causal).sum())
+
+        def head():
+            orc.forward_head(qh, kh, vh, w.scale, w.causal, block_mask=mh)
+            orc.backward_head(qh, kh, vh, doh, w.scale, w.causal, block_mask=mh)
+
+        out["cpu_baseline"] = timed_oracle(head, 3.5 * 4.0 * d * pairs0, "TFLOP/s", args.cpu_seconds,
+                                           f"head (0, 0) with its block mask, N={N} d={d}, forward + backward in fp64 "
+                                           "(dense S and P, masked entries -inf)")
     print(json.dumps(out), flush=True)
     return 0
 
@@ -449,6 +493,14 @@ def bench_fp8(args, w):
                      "traffic": measured_traffic("fwd_fp8", w.name + "_fp8") if (B, H) == (2, 32) else None,
                      "avg_launch_ms": round(t_fp8, 4)},
     }
+    if not args.no_cpu_baseline:
+        from oracle import fp8 as orc8
+
+        qh, kh, vh = (inp[x][0, 0].numpy() for x in ("q8", "k8", "v8"))
+        out["cpu_baseline"] = timed_oracle(
+            lambda: orc8.forward_head_fp8(qh, kh, vh, inp["dq"], inp["dk"], inp["dv"], w.scale, w.causal),
+            F / (B * H), "TFLOP/s", args.cpu_seconds,
+            f"head (0, 0), N={N} d={d}, e4m3 codes dequantized to fp64, forward with S and P materialised")
     print(json.dumps(out), flush=True)
     return 0
 
