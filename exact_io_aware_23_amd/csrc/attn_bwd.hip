@@ -36,6 +36,8 @@
 // delta = sum_j P_ij dP_ij in fp32 from the same P and dP it forms, and dkdv
 // runs after it with that exact delta.  Order: preprocess -> dq -> dkdv.
 // Both recompute P with p = exp2(s * scale * log2 e - L * log2 e).
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -361,7 +363,12 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
               uint32_t seed_lo, uint32_t seed_hi, float inv_keep) {
   using C = DqCfg<D>;
   static_assert(!(SPARSE && DROP), "block-sparse and dropout are separate entry points");
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
+  // one array per stage: the compiler then knows that reads of one stage do
+  // not alias the buffer -> LDS copies into the other, and does not wait for
+  // those copies before the reads
+  __shared__ __attribute__((aligned(16))) bf16 kv_lds0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 kv_lds1[C::STAGE];
+  auto stage_lds = [&](int stage) -> bf16* { return stage ? kv_lds1 : kv_lds0; };
   // block-sparse: the key tiles of this query block whose 128 x 128 block is on
   __shared__ uint16_t tlist[SPARSE ? kMaxSparseN / C::BC : 1];
   __shared__ int wcnt[SPARSE ? 4 : 1];
@@ -423,7 +430,7 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
     toff[i] = (row * D + 8 * (cphys ^ chunk_swz<C::NCH>(row))) * 2;
   }
   auto load_tile = [&](int kv0, int stage) {
-    bf16* Ks = smem + stage * C::STAGE;
+    bf16* Ks = stage_lds(stage);
 #pragma unroll
     for (int i = 0; i < C::NB; ++i) {
       const int b = wave * C::NB + i;
@@ -453,15 +460,17 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
   wait_vmem_all();
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
+  // iteration j works on stage j & 1, passed as a constant (the loop is
+  // unrolled by two) so every LDS access names one array
+  auto iter = [&](int j, auto stage_c) {
+    constexpr int stage = decltype(stage_c)::value;
     int raw2 = 0;
     if constexpr (SPARSE) raw2 = tlist[min(j + 2, kMaxSparseN / C::BC - 1)];
-    const int stage = j & 1;
     const int kv0 = kv_cur;
     if (j + 1 < n_tiles) load_tile(kv_nxt, stage ^ 1);
 
     if (j < wave_tiles) {
-      const bf16* Ks = smem + stage * C::STAGE;
+      const bf16* Ks = stage_lds(stage);
       const bf16* Vs = Ks + C::TILE;
       // ---- S^T = K Q^T and dP^T = V dO^T (K, V rows read in swap23 order)
       f32x16 st, dpt;
@@ -513,7 +522,13 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
     kv_cur = kv_nxt;
     if constexpr (SPARSE) kv_nxt = j + 2 < n_tiles ? uniform(raw2) * C::BC : 0;
     else kv_nxt = (j + 2) * C::BC;
+  };
+  int j = 0;
+  for (; j + 1 < n_tiles; j += 2) {
+    iter(j, std::integral_constant<int, 0>{});
+    iter(j + 1, std::integral_constant<int, 1>{});
   }
+  if (j < n_tiles) iter(j, std::integral_constant<int, 0>{});
 
   // exact delta_q = sum_j P_qj dP_qj, handed to the dK/dV kernel
   d_exact = pair_sum(d_exact);
