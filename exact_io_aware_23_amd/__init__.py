@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     AttnError,
     LIB_PATH,
     abi_version,
+    attention,
     bwd,
     bwd_block_sparse,
     bwd_dkdv,

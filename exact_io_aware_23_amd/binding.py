@@ -333,3 +333,27 @@ def bwd_dq(q, k, v, lse, do, delta, scale: float | None = None, causal: bool = F
           delta.data_ptr(), dq.data_ptr(), delta_out.data_ptr(), B, H, N, d, _dtype_code(q),
           _default_scale(d, scale), int(bool(causal)), _stream(q.device))
     return dq, delta_out
+
+
+class _Attention(torch.autograd.Function):
+    """attn_fwd in the forward (saving O and L), attn_bwd in the backward."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, scale, causal):
+        o, lse = fwd(q, k, v, scale=scale, causal=causal)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.scale, ctx.causal = scale, causal
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, lse, do.to(q.dtype).contiguous(), scale=ctx.scale, causal=ctx.causal)
+        return dq, dk, dv, None, None
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float | None = None, causal: bool = False):
+    """O = softmax(scale Q K^T + mask) V on [B, H, N, d] tensors, differentiable
+    with respect to q, k and v through attn_bwd (bf16 only; the fp32 forward
+    has no backward and raises there)."""
+    return _Attention.apply(q, k, v, _default_scale(q.shape[-1], scale), bool(causal))

@@ -256,3 +256,13 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         binding.fwd(q, q, q)
+
+
+def test_autograd_wrapper_refuses_cpu_tensors():
+    import torch
+
+    from exact_io_aware_23_amd import attention
+
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attention(q, q, q)
