@@ -10,6 +10,8 @@ forward alone.
                     [--batch B] [--heads H] [--no-cpu-baseline]
                     [--block-density P] [--dropout P] [--fp8] [--decode NQ [--decode-nk NK]]
 
+--flush-l2 writes a 512 MiB scratch buffer before every step (outside the timed
+kernels), so the inputs start from HBM; value then uses the kernels' event times.
 --block-density P times the block-sparse entry points instead, on a seeded
 random mask over 128 x 128 blocks (each block on with probability P, diagonal
 blocks always on), counting only the allowed (query, key) pairs.
@@ -72,6 +74,8 @@ def parse():
     ap.add_argument("--fp8", action="store_true", help="time attn_fwd_fp8 (e4m3 inputs) on the workload's shape")
     ap.add_argument("--decode", type=int, default=None, help="time attn_decode with this many queries per head")
     ap.add_argument("--decode-nk", type=int, default=16384, help="cached keys per head for --decode")
+    ap.add_argument("--flush-l2", action="store_true",
+                    help="write a 512 MiB scratch buffer before every step, so no input is left in L2 or the MALL")
     ap.add_argument("--block-density", type=float, default=None,
                     help="time attn_fwd_block_sparse + attn_bwd_block_sparse on a random block mask of this density")
     return ap.parse_args()
@@ -134,6 +138,7 @@ def cpu_baseline(w: W.Workload, budget_s: float):
 
 
 COPY_BYTES = 1 << 30
+FLUSH_BYTES = 512 << 20
 
 
 def copy_calibration(args):
@@ -543,8 +548,11 @@ def main():
     delta_exact = torch.empty_like(delta)
     stream = torch.cuda.current_stream(dev)
     names = ["fwd", "preprocess", "dq", "dkdv"]
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if args.flush_l2 else None
 
     def step(ev=None):
+        if scratch is not None:
+            scratch.fill_(1.0)  # outside the timed kernels: evicts the inputs from L2 and the MALL
         if ev is not None:
             ev[0].record(stream)
         A.fwd(q, k, v, scale=w.scale, causal=w.causal, out=o, lse=lse)
@@ -577,13 +585,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per_kernel = {n: 0.0 for n in names}
-    for ev in events:
-        for j, n in enumerate(names):
-            per_kernel[n] += ev[j].elapsed_time(ev[j + 1])
-    per_kernel = {n: t / args.steps for n, t in per_kernel.items()}  # ms per launch
+    samples = {n: [ev[j].elapsed_time(ev[j + 1]) for ev in events] for j, n in enumerate(names)}
+    per_kernel = {n: sum(t) / args.steps for n, t in samples.items()}  # ms per launch
     gpu_ms = events[0][0].elapsed_time(events[-1][4]) / args.steps
     ms_per_step = wall * 1e3 / args.steps
+    if scratch is not None:  # the flush writes sit between the steps: time the kernels only
+        ms_per_step = sum(per_kernel.values())
 
     F_fwd, F_bwd = w.fwd_flops(), w.bwd_flops()
     if fwd_only:
@@ -622,13 +629,15 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-                   "pass": "fwd" if fwd_only else "fwd+bwd"},
+                   "pass": "fwd" if fwd_only else "fwd+bwd", **({"flush_l2_bytes": FLUSH_BYTES} if args.flush_l2 else {})},
         "fwd_tflops": round(fwd_tflops, 2),
         "fwd_frac_mfma_peak": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "bwd_tflops": round(bwd_tflops, 2) if bwd_tflops else None,
         "fwdbwd_frac_mfma_peak": round(value / MFMA_BF16_PEAK_TFLOPS, 4),
         "gpu_ms_per_step": round(gpu_ms, 4),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
+        "kernel_ms_median": {n: round(sorted(t)[len(t) // 2], 4) for n, t in samples.items()},
+        "kernel_ms_min": {n: round(min(t), 4) for n, t in samples.items()},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
