@@ -250,14 +250,21 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
       const float* Ls = Fs + stage * 64;
       const float* Ds = Ls + 32;
       // ---- S = Q K^T and dP = dO V^T
+      // Each MFMA's operands are read one MFMA ahead; sched_barrier fences
+      // the steps so the compiler cannot pull the reads down to their use.
       f32x16 s, dp;
+      bf16x8 aq = lds_read16(Qs + a_row * D, g ^ a_swz);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        const bf16x8 aq = lds_read16(Qs + a_row * D, (2 * ks + g) ^ a_swz);
-        s = mfma32(aq, kreg[ks], ks == 0 ? f32x16{} : s);
         const bf16x8 ao = lds_read16(dOs + a_row * D, (2 * ks + g) ^ a_swz);
         const bf16x8 bv = lds_read16(Vs + v_row * D, (2 * ks + g) ^ v_swz);
+        __builtin_amdgcn_sched_barrier(0);
+        s = mfma32(aq, kreg[ks], ks == 0 ? f32x16{} : s);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + 1 < C::KS) aq = lds_read16(Qs + a_row * D, (2 * ks + 2 + g) ^ a_swz);
+        __builtin_amdgcn_sched_barrier(0);
         dp = mfma32(ao, bv, ks == 0 ? f32x16{} : dp);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // ---- P = exp2(s c - L'), dS = P (dP - delta); query of register r: crow(r, g)
       // masked scores become -inf, so exp2 gives exactly 0 (one branch per tile)
@@ -278,35 +285,85 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 #pragma unroll
         for (int r = 0; r < 16; ++r) kept[r] = drop_keep(word, r, drop_t);
       }
+      if constexpr (DROP) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int v4 = 0; v4 < 2; ++v4) {
-          const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + 16 * h + 8 * g + 4 * v4);
-          const f32x4 dv4 = *reinterpret_cast<const f32x4*>(Ds + 16 * h + 8 * g + 4 * v4);
+          for (int v4 = 0; v4 < 2; ++v4) {
+            const f32x4 lv = *reinterpret_cast<const f32x4*>(Ls + 16 * h + 8 * g + 4 * v4);
+            const f32x4 dv4 = *reinterpret_cast<const f32x4*>(Ds + 16 * h + 8 * g + 4 * v4);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 8 * h + 4 * v4 + i;
-            const float p = fast_exp2(fmaf(s[r], c, -lv[i]));
-            if constexpr (DROP) {
+            for (int i = 0; i < 4; ++i) {
+              const int r = 8 * h + 4 * v4 + i;
+              const float p = fast_exp2(fmaf(s[r], c, -lv[i]));
               const float dpr = kept[r] ? dp[r] * inv_keep : 0.f;
               s[r] = kept[r] ? p * inv_keep : 0.f;
               dp[r] = p * (dpr - dv4[i]);
-            } else {
-              s[r] = p;
-              dp[r] = p * (dp[r] - dv4[i]);
             }
           }
+        // ---- dV^T += dO^T P and dK^T += Q^T dS (A operands by transposing reads)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bf16x8 pop = c_to_operand(s, h);
+          const bf16x8 dso = c_to_operand(dp, h);
+#pragma unroll
+          for (int dt = 0; dt < C::DT; ++dt) {
+            dv[dt] = mfma32(tr_operand<D>(dOs, dt, h, trb), pop, dv[dt]);
+            dk[dt] = mfma32(tr_operand<D>(Qs, dt, h, trb), dso, dk[dt]);
+          }
         }
-      // ---- dV^T += dO^T P and dK^T += Q^T dS (A operands by transposing reads)
+      } else {
+        // The elementwise work of the first half (registers r < 8), then the
+        // dV / dK MFMAs in a fixed order: each one's transposing reads are
+        // issued one MFMA ahead, and the second half's elementwise work is
+        // spread over the first half's MFMAs (sched_barrier fences the steps).
+        auto stat4 = [&](const float* base, int r) {
+          return *reinterpret_cast<const f32x4*>(base + 16 * (r / 8) + 8 * g + 4 * ((r / 4) % 2));
+        };
+        auto elem = [&](int r, const f32x4& lv, const f32x4& dl) {
+          const float p = fast_exp2(fmaf(s[r], c, -lv[r % 4]));
+          s[r] = p;
+          dp[r] = p * (dp[r] - dl[r % 4]);
+        };
+        f32x4 la = stat4(Ls, 0), da = stat4(Ds, 0), lb = stat4(Ls, 4), db = stat4(Ds, 4);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const bf16x8 pop = c_to_operand(s, h);
-        const bf16x8 dso = c_to_operand(dp, h);
+        for (int r = 0; r < 4; ++r) elem(r, la, da);
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) {
-          dv[dt] = mfma32(tr_operand<D>(dOs, dt, h, trb), pop, dv[dt]);
-          dk[dt] = mfma32(tr_operand<D>(Qs, dt, h, trb), dso, dk[dt]);
+        for (int r = 4; r < 8; ++r) elem(r, lb, db);
+        la = stat4(Ls, 8);
+        da = stat4(Ds, 8);
+        lb = stat4(Ls, 12);
+        db = stat4(Ds, 12);
+        bf16x8 pop = c_to_operand(s, 0), dso = c_to_operand(dp, 0);
+        // MFMA i: dV (i even) or dK (i odd), d tile (i / 2) % DT, half i / (2 DT)
+        constexpr int NM = 4 * C::DT;
+        constexpr int EPM = 8 / (2 * C::DT);  // second-half elements per first-half MFMA
+        auto operand = [&](int i) {
+          return tr_operand<D>((i & 1) ? Qs : dOs, (i / 2) % C::DT, i / (2 * C::DT), trb);
+        };
+        bf16x8 nxt = operand(0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          const bf16x8 cur = nxt;
+          if (i + 1 < NM) nxt = operand(i + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i == 2 * C::DT) {
+            pop = c_to_operand(s, 1);
+            dso = c_to_operand(dp, 1);
+          }
+          const int dt = (i / 2) % C::DT;
+          if (i & 1) dk[dt] = mfma32(cur, dso, dk[dt]);
+          else dv[dt] = mfma32(cur, pop, dv[dt]);
+          if (i < 2 * C::DT) {
+#pragma unroll
+            for (int e = 0; e < EPM; ++e) {
+              const int r = 8 + EPM * i + e;
+              if (r < 12) elem(r, la, da);
+              else elem(r, lb, db);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -498,21 +555,35 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
 #pragma unroll
         for (int r = 0; r < 16; ++r) dpt[r] = drop_keep(word, r, drop_t) ? dpt[r] * inv_keep : 0.f;
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(st[r], c, -lq));
-        d_exact = fmaf(p, dpt[r], d_exact);
-        dpt[r] = p * (dpt[r] - dq_delta);
-        st[r] = p;
-      }
-      // ---- dQ^T += K^T dS^T, K^T by transposing reads
+      // per half h of the tile's keys: P, the exact-delta partial sums and
+      // dS = P (dP - delta~), then dQ^T += K^T dS^T for those 16 keys
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int r = 8 * h; r < 8 * h + 8; ++r) {
+          const float p = fast_exp2(fmaf(st[r], c, -lq));
+          d_exact = fmaf(p, dpt[r], d_exact);
+          dpt[r] = p * (dpt[r] - dq_delta);
+          st[r] = p;
+        }
         const bf16x8 dso = c_to_operand(dpt, h);
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          const bf16x8 akt = tr_operand<D>(Ks, dt, h, trb);
+          const bf16x8 akt = tr_operand<D>(Ks, dt, h, trb);  // K^T by transposing reads
           dq[dt] = mfma32(akt, dso, dq[dt]);
+        }
+      }
+      if constexpr (!DROP) {
+        // Instruction order: the first half's VALU work, then each dQ MFMA
+        // with the transposing reads of the next one, the second half's
+        // exponentials spread over the first half's MFMAs.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 44, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * C::DT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < 2 * C::DT - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          if (i < C::DT) __builtin_amdgcn_sched_group_barrier(0x402, 11, 0);
         }
       }
     }

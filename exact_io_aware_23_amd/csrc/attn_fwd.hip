@@ -38,6 +38,10 @@
 //     skips the tiles past its own last row; only diagonal (and ragged tail)
 //     tiles apply the mask.  Query tiles run longest first within a head, and
 //     work items are renumbered so each XCD sweeps whole heads (L2 reuse).
+//   * Short sequences at d = 64 (N <= 512, a few tiles per workgroup) take a
+//     variant without the in-wave pipeline: one score tile in registers, 122
+//     VGPRs, four workgroups per CU, so more workgroups have loads in flight
+//     in a regime where HBM latency, not the matrix cores, sets the time.
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -63,8 +67,12 @@ struct FwdCfg {
 // 2^kTau; the result is unchanged (the same m is used for O and l).
 constexpr float kTau = 8.0f;
 
-template <int D, bool CAUSAL, bool SPARSE, bool DROP>
-__global__ void __launch_bounds__(256, 2)
+// Longest sequence (d = 64, no block mask, no dropout) that the forward runs
+// with the one-tile-at-a-time kernel: up to eight 64-key tiles per workgroup.
+constexpr int kShortSeqMaxN = 512;
+
+template <int D, bool CAUSAL, bool SPARSE, bool DROP, bool PIPE = true>
+__global__ void __launch_bounds__(256, PIPE ? 2 : 4)
 fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                 bf16* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, int total, float c,
                 const uint8_t* __restrict__ Mask, int mask_hs, int nb, uint32_t drop_t, uint32_t seed_lo,
@@ -286,66 +294,100 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     }
   };
 
-  // ---- software pipeline.  Slot s of LDS holds K and V tiles of the same
-  // parity.  Iteration j reads K(j+1) (scores of the next tile) and V(j) (this
-  // tile's P V), and loads K(j+2) over K(j) and V(j+1) over V(j-1), both read
-  // before the previous barrier.  The scores of tile j+1 are independent of
-  // tile j's exponentials, and tile j's P V of tile j+1's max, so each pair
-  // sits in one basic block for the scheduler to interleave.
-  const int kv_first = kv0_of(0);
-  if (n_tiles > 0) {
-    load_k(kv_first, 0);
-    load_v(kv_first, 0);
-  }
-  if (n_tiles > 1) load_k(kv0_of(1), 1);
-  wait_vmem_all();
-  __syncthreads();
-  f32x16 sa[2], sb[2];
-  if (wave_tiles > 0) {
-    scores(0, sa);
-    if (needs_mask(kv_first)) mask(sa, kv_first);
-    rescale(tile_max(sa));
-  }
-  // first keys of tiles j+1 and j+2 at the start of step j, carried from step
-  // to step; a block-sparse step reads the entry for j+3 from the LDS list
-  // early and makes it scalar only after its barrier, when no other LDS read
-  // is outstanding
-  int kv_a = kv0_of(1), kv_b = kv0_of(2);
-  __syncthreads();  // every wave has read K(0) before K(2) is loaded over it
-
-  // `par` = j & 1, passed as a literal so every LDS address is a constant
-  // offset from one per-lane base
-  auto step = [&](int j, int par, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    int raw3 = 0;
-    if constexpr (SPARSE) raw3 = tlist[min(j + 3, kMaxSparseN / C::BC - 1)];
-    if (j + 2 < n_tiles) load_k(kv_b, par);
-    if (j + 1 < n_tiles) load_v(kv_a, par ^ 1);
-    if (j < wave_tiles) {
-      // The scores of tile j+1 are formed even when this wave has no such
-      // tile: the slot then holds another K tile (in bounds), every one of
-      // its keys lies past this wave's rows or past N, so the mask sets them
-      // all to -inf, and the rescale is skipped.  One code path per step.
-      bf16x8 pop[4];
-      scores(par ^ 1, nxt);
-      exps(cur, pop, j * C::BC);  // (dropout runs on dense tiles only, so tile j starts at key 64 j)
-      pv(par, pop);
-      pin_a();
-      pin_b();
-      if (needs_mask(kv_a)) mask(nxt, kv_a);
-      if (j + 1 < wave_tiles) rescale(tile_max(nxt));
+  if constexpr (!PIPE) {
+    // Short sequences (a few tiles per workgroup): one tile at a time, scores,
+    // max, exponentials and P V, while the next tile's K and V are copied into
+    // the other LDS slot.  One score tile instead of two keeps the kernel
+    // under 128 VGPRs, so four workgroups share a CU and more of them have
+    // loads in flight.
+    if (n_tiles > 0) {
+      load_k(kv0_of(0), 0);
+      load_v(kv0_of(0), 0);
     }
-    wait_vmem_all();  // K(j+2) and V(j+1) have landed in LDS
+    wait_vmem_all();
     __syncthreads();
-    kv_a = kv_b;
-    if constexpr (SPARSE) kv_b = j + 3 < n_tiles ? uniform(raw3) * C::BC : N;
-    else kv_b = (j + 3) * C::BC;
-  };
-  int j = 0;
-  for (; j + 1 < n_tiles; j += 2) {
-    step(j, 0, sa, sb);
-    step(j + 1, 1, sb, sa);
+    for (int j = 0; j < n_tiles; ++j) {
+      const int slot = j & 1;
+      const int kv0 = kv0_of(j);
+      if (j + 1 < n_tiles) {
+        load_k(kv0_of(j + 1), slot ^ 1);
+        load_v(kv0_of(j + 1), slot ^ 1);
+      }
+      if (j < wave_tiles) {
+        f32x16 st[2];
+        bf16x8 pop[4];
+        scores(slot, st);
+        if (needs_mask(kv0)) mask(st, kv0);
+        rescale(tile_max(st));
+        exps(st, pop, kv0);
+        pv(slot, pop);
+      }
+      wait_vmem_all();  // tile j+1 has landed; every wave is done with slot j & 1
+      __syncthreads();
+    }
+  } else {
+  // ---- software pipeline.  Slot s of LDS holds K and V tiles of the same
+    // parity.  Iteration j reads K(j+1) (scores of the next tile) and V(j) (this
+    // tile's P V), and loads K(j+2) over K(j) and V(j+1) over V(j-1), both read
+    // before the previous barrier.  The scores of tile j+1 are independent of
+    // tile j's exponentials, and tile j's P V of tile j+1's max, so each pair
+    // sits in one basic block for the scheduler to interleave.
+    const int kv_first = kv0_of(0);
+    if (n_tiles > 0) {
+      load_k(kv_first, 0);
+      load_v(kv_first, 0);
+    }
+    if (n_tiles > 1) load_k(kv0_of(1), 1);
+    wait_vmem_all();
+    __syncthreads();
+    f32x16 sa[2], sb[2];
+    if (wave_tiles > 0) {
+      scores(0, sa);
+      if (needs_mask(kv_first)) mask(sa, kv_first);
+      rescale(tile_max(sa));
+    }
+    // first keys of tiles j+1 and j+2 at the start of step j, carried from step
+    // to step; a block-sparse step reads the entry for j+3 from the LDS list
+    // early and makes it scalar only after its barrier, when no other LDS read
+    // is outstanding
+    int kv_a = kv0_of(1), kv_b = kv0_of(2);
+    __syncthreads();  // every wave has read K(0) before K(2) is loaded over it
+  
+    // `par` = j & 1, passed as a literal so every LDS address is a constant
+    // offset from one per-lane base
+    auto step = [&](int j, int par, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+      int raw3 = 0;
+      if constexpr (SPARSE) raw3 = tlist[min(j + 3, kMaxSparseN / C::BC - 1)];
+      if (j + 2 < n_tiles) load_k(kv_b, par);
+      if (j + 1 < n_tiles) load_v(kv_a, par ^ 1);
+      if (j < wave_tiles) {
+        // The scores of tile j+1 are formed even when this wave has no such
+        // tile: the slot then holds another K tile (in bounds), every one of
+        // its keys lies past this wave's rows or past N, so the mask sets them
+        // all to -inf, and the rescale is skipped.  One code path per step.
+        bf16x8 pop[4];
+        scores(par ^ 1, nxt);
+        exps(cur, pop, j * C::BC);  // (dropout runs on dense tiles only, so tile j starts at key 64 j)
+        pv(par, pop);
+        pin_a();
+        pin_b();
+        if (needs_mask(kv_a)) mask(nxt, kv_a);
+        if (j + 1 < wave_tiles) rescale(tile_max(nxt));
+      }
+      wait_vmem_all();  // K(j+2) and V(j+1) have landed in LDS
+      __syncthreads();
+      kv_a = kv_b;
+      if constexpr (SPARSE) kv_b = j + 3 < n_tiles ? uniform(raw3) * C::BC : N;
+      else kv_b = (j + 3) * C::BC;
+    };
+    int j = 0;
+    for (; j + 1 < n_tiles; j += 2) {
+      step(j, 0, sa, sb);
+      step(j + 1, 1, sb, sa);
+    }
+    if (j < n_tiles) step(j, 0, sa, sb);
+  
   }
-  if (j < n_tiles) step(j, 0, sa, sb);
 
   // ---- epilogue: O = O_acc / l, L = (m + log2 l) ln 2; a row with no allowed
   // key (possible only under a block mask) gets O = 0 and L = -inf
@@ -444,6 +486,11 @@ hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* 
   static_assert(C::BR == kMaskBlock, "a workgroup owns one block row of the mask");
   const int n_qtiles = (N + C::BR - 1) / C::BR;
   const int total = BH * n_qtiles;
+  // the one-tile-at-a-time kernel for short sequences exists for d = 64 only
+  // (at d = 128 the pipelined kernel's state already limits a CU to two
+  // workgroups by LDS as well as registers)
+  constexpr bool kShortFwd = D == 64;
+  const bool short_seq = kShortFwd && N <= kShortSeqMaxN;
   if (m.ptr)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, false>), dim3(total), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
@@ -452,6 +499,10 @@ hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* 
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, true>), dim3(total), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
                        scale * kLog2e, (const uint8_t*)nullptr, 0, 0, dr.t, dr.seed_lo, dr.seed_hi, dr.inv_keep);
+  else if (short_seq)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, false, /*PIPE=*/!kShortFwd>), dim3(total), dim3(256), 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
+                       scale * kLog2e, (const uint8_t*)nullptr, 0, 0, 0u, 0u, 0u, 1.f);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, false>), dim3(total), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,

@@ -96,6 +96,8 @@ SMALL = [
     (1, 2, 1, 64, False), (1, 2, 1, 128, True), (1, 2, 17, 64, True), (2, 3, 200, 64, False),
     (1, 2, 333, 128, True), (1, 2, 512, 128, False), (2, 2, 1000, 128, True), (1, 3, 257, 64, True),
     (1, 2, 640, 64, False), (1, 1, 129, 128, False), (1, 2, 1100, 64, True),
+    # the last length the one-tile-at-a-time d=64 forward takes, and the first past it
+    (1, 2, 512, 64, True), (1, 2, 513, 64, False),
 ]
 
 
