@@ -1,6 +1,7 @@
 """Benchmark of the fused exact attention (forward + backward) on one MI355X.
 
-One step = attn_fwd followed by the backward stages (preprocess, dq, dkdv) on
+One step = attn_fwd followed by the backward stages attn_bwd runs (the dq stage,
+which also forms delta~ = rowsum(dO O), then dkdv) on
 one batch of the headline workload, B=2, H=32, N=8192, d=128, bf16, causal,
 with inputs already resident in device memory.  Prints one JSON line.
 Workloads without a backward pass (fp32_small, bf16_n256_d64_short) time the
@@ -88,7 +89,8 @@ def kernel_flops(w: W.Workload):
     2*B*H*N^2*d (halved when causal); the forward has two, the backward five
     (the recomputed Q K^T, dO V^T, P^T dO, dS^T Q and dS K).  dkdv executes four
     of the five; dq executes dS K (its recomputed Q K^T and dO V^T are not
-    counted); preprocess is memory traffic only.
+    counted); the preprocess stage (folded into dq by attn_bwd) is memory
+    traffic only.
     """
     one = w.fwd_flops() / 2
     return {"fwd": 2 * one, "dkdv": 4 * one, "dq": 1 * one, "preprocess": 0.0}
@@ -329,7 +331,7 @@ def bench_dropout(args, w):
                    "dropout": args.dropout, "seed": seed},
         "fwd_tflops": round(achieved, 2),
         "bwd_tflops": round(F_bwd / (t_bwd * 1e-3) / 1e12, 2),
-        "kernel_ms": {"fwd": round(t_fwd, 4), "bwd (preprocess+dq+dkdv)": round(t_bwd, 4)},
+        "kernel_ms": {"fwd": round(t_fwd, 4), "bwd (dq+dkdv)": round(t_bwd, 4)},
         "roofline": {"kernel": "fwd", "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "avg_launch_ms": round(t_fwd, 4)},
@@ -415,7 +417,7 @@ def bench_block_sparse(args, w):
                    "mask": "random 128x128 blocks, torch seed 1234, diagonal blocks on"},
         "fwd_tflops": round(achieved, 2),
         "bwd_tflops": round(F_bwd / (t_bwd * 1e-3) / 1e12, 2),
-        "kernel_ms": {"fwd": round(t_fwd, 4), "bwd (preprocess+dq+dkdv)": round(t_bwd, 4)},
+        "kernel_ms": {"fwd": round(t_fwd, 4), "bwd (dq+dkdv)": round(t_bwd, 4)},
         "roofline": {"kernel": "fwd", "bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "avg_launch_ms": round(t_fwd, 4)},
@@ -544,10 +546,9 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    delta_exact = torch.empty_like(delta)
+    delta_exact = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    names = ["fwd", "preprocess", "dq", "dkdv"]
+    names = ["fwd", "dq", "dkdv"]  # the launches attn_bwd makes: the dq stage forms delta~ itself
     scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if args.flush_l2 else None
 
     def step(ev=None):
@@ -563,21 +564,18 @@ def main():
                 for e in ev[2:]:
                     e.record(stream)
             return
-        A.bwd_preprocess(o, do, delta)
+        A.bwd_dq_fused(q, k, v, o, lse, do, scale=w.scale, causal=w.causal, dq=dq, delta_out=delta_exact)
         if ev is not None:
             ev[2].record(stream)
-        A.bwd_dq(q, k, v, lse, do, delta, scale=w.scale, causal=w.causal, dq=dq, delta_out=delta_exact)
-        if ev is not None:
-            ev[3].record(stream)
         A.bwd_dkdv(q, k, v, lse, do, delta_exact, scale=w.scale, causal=w.causal, dk=dk, dv=dv)
         if ev is not None:
-            ev[4].record(stream)
+            ev[3].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -587,7 +585,7 @@ def main():
 
     samples = {n: [ev[j].elapsed_time(ev[j + 1]) for ev in events] for j, n in enumerate(names)}
     per_kernel = {n: sum(t) / args.steps for n, t in samples.items()}  # ms per launch
-    gpu_ms = events[0][0].elapsed_time(events[-1][4]) / args.steps
+    gpu_ms = events[0][0].elapsed_time(events[-1][len(names)]) / args.steps
     ms_per_step = wall * 1e3 / args.steps
     if scratch is not None:  # the flush writes sit between the steps: time the kernels only
         ms_per_step = sum(per_kernel.values())
@@ -597,7 +595,7 @@ def main():
         F_bwd = 0.0
     value = (F_fwd + F_bwd) / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = F_fwd / (per_kernel["fwd"] * 1e-3) / 1e12
-    bwd_ms = per_kernel["preprocess"] + per_kernel["dq"] + per_kernel["dkdv"]
+    bwd_ms = per_kernel["dq"] + per_kernel["dkdv"]
     bwd_tflops = F_bwd / (bwd_ms * 1e-3) / 1e12 if bwd_ms > 0 and F_bwd > 0 else None
 
     kf = kernel_flops(w)

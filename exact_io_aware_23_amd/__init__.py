@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     bwd_dkdv,
     bwd_dropout,
     bwd_dq,
+    bwd_dq_fused,
     bwd_preprocess,
     bwd_workspace_bytes,
     decode,

@@ -30,6 +30,7 @@ _SIGNATURES = {
     "attn_bwd_preprocess": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_dq_fused": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_fwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _S, _I, _I, _I, _I, _I, _F,
                                    _I, _P]),
@@ -332,6 +333,21 @@ def bwd_dq(q, k, v, lse, do, delta, scale: float | None = None, causal: bool = F
     _call("attn_bwd_dq", q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
           delta.data_ptr(), dq.data_ptr(), delta_out.data_ptr(), B, H, N, d, _dtype_code(q),
           _default_scale(d, scale), int(bool(causal)), _stream(q.device))
+    return dq, delta_out
+
+
+def bwd_dq_fused(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, dq=None, delta_out=None):
+    """attn_bwd_dq_fused (preprocess and dq in one launch); returns (dQ, exact delta)."""
+    B, H, N, d = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    delta_out = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta_out is None else delta_out
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    _check("lse", lse, (B, H, N), torch.float32)
+    _check("delta_out", delta_out, (B, H, N), torch.float32)
+    _call("attn_bwd_dq_fused", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+          dq.data_ptr(), delta_out.data_ptr(), B, H, N, d, _dtype_code(q), _default_scale(d, scale),
+          int(bool(causal)), _stream(q.device))
     return dq, delta_out
 
 

@@ -54,7 +54,7 @@ size_t delta_bytes(int B, int H, int N) {
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
   if (!sizes_ok(B, H, N)) return 0;
-  return 2 * delta_bytes(B, H, N);  // approximate delta, then exact delta
+  return delta_bytes(B, H, N);  // the exact delta, from the dq stage to the dkdv stage
 }
 
 attn_status_t attn_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int H, int N, int d,
@@ -87,23 +87,33 @@ attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const flo
   if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
   const attn_status_t s = check_bf16_d(d, dtype);
   if (s != ATTN_OK) return s;
-  return map_hip(attn::launch_bwd_dq(q, k, v, lse, dout, delta, dq, delta_out, B * H, N, d, scale,
+  return map_hip(attn::launch_bwd_dq(q, k, v, lse, dout, delta, nullptr, dq, delta_out, B * H, N, d, scale,
+                                     causal != 0, attn::BlockMask{}, attn::DropParams{}, (hipStream_t)stream));
+}
+
+attn_status_t attn_bwd_dq_fused(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                const void* dout, void* dq, float* delta_out, int B, int H, int N, int d,
+                                attn_dtype_t dtype, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !delta_out) return ATTN_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
+  const attn_status_t s = check_bf16_d(d, dtype);
+  if (s != ATTN_OK) return s;
+  return map_hip(attn::launch_bwd_dq(q, k, v, lse, dout, nullptr, o, dq, delta_out, B * H, N, d, scale,
                                      causal != 0, attn::BlockMask{}, attn::DropParams{}, (hipStream_t)stream));
 }
 
 namespace {
-// preprocess -> dq (also writes the exact delta) -> dkdv, with an optional block mask
+// dq (forms delta~ = rowsum(dO * O) itself, bit for bit as the preprocess
+// stage does, and writes the exact delta) -> dkdv, with an optional block mask
 attn_status_t bwd_all(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dout, void* dq, void* dk, void* dv, void* workspace, int B, int H, int N,
                       int d, float scale, int causal, const attn::BlockMask& m, const attn::DropParams& dr,
                       void* stream) {
-  float* delta_approx = static_cast<float*>(workspace);
-  float* delta_exact = reinterpret_cast<float*>(static_cast<char*>(workspace) + delta_bytes(B, H, N));
+  float* delta_exact = static_cast<float*>(workspace);
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = attn::launch_bwd_preprocess(o, dout, delta_approx, B * H, N, d, st);
-  if (e != hipSuccess) return ATTN_ERR_HIP;
-  e = attn::launch_bwd_dq(q, k, v, lse, dout, delta_approx, dq, delta_exact, B * H, N, d, scale, causal != 0,
-                          m, dr, st);
+  hipError_t e = attn::launch_bwd_dq(q, k, v, lse, dout, nullptr, o, dq, delta_exact, B * H, N, d, scale,
+                                     causal != 0, m, dr, st);
   if (e != hipSuccess) return ATTN_ERR_HIP;
   e = attn::launch_bwd_dkdv(q, k, v, lse, dout, delta_exact, dk, dv, B * H, N, d, scale, causal != 0, m, dr, st);
   return map_hip(e);

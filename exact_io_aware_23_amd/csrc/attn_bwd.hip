@@ -415,7 +415,7 @@ template <int D, bool CAUSAL, bool SPARSE, bool DROP>
 __global__ void __launch_bounds__(256, 2)
 bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
               const float* __restrict__ Lse, const bf16* __restrict__ dO, const float* __restrict__ Delta,
-              bf16* __restrict__ dQ, float* __restrict__ DeltaOut, int N, int n_qtiles, int total, float c,
+              const bf16* __restrict__ Ofused, bf16* __restrict__ dQ, float* __restrict__ DeltaOut, int N, int n_qtiles, int total, float c,
               float scale, const uint8_t* __restrict__ Mask, int mask_hs, int nb, uint32_t drop_t,
               uint32_t seed_lo, uint32_t seed_hi, float inv_keep) {
   using C = DqCfg<D>;
@@ -459,7 +459,30 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
   // rows past N, and rows with no allowed key (L = -inf), get p = exp2(-inf) = 0
   const float lrow = q < N ? Lse[(size_t)bh * N + q] : -INFINITY;
   const float lq = lrow == -INFINITY ? INFINITY : lrow * kLog2e;
-  const float dq_delta = q < N ? Delta[(size_t)bh * N + q] : 0.f;  // rowsum(dO * O), O as stored
+  // delta~ = rowsum(dO * O) with O as stored: read from Delta (written by the
+  // preprocess kernel) or, when O is passed, formed here in that kernel's
+  // exact summation order (an FMA chain over each 16-byte chunk, then the same
+  // pairwise tree over the chunks), so both routes give the same bits
+  float dq_delta = 0.f;
+  if (Ofused != nullptr) {
+    const rsrc_t rO = make_rsrc(Ofused + head, head_bytes);
+    float cs[C::KS];  // chunk 2 ks + g of the row
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 ov = __builtin_bit_cast(bf16x8, bload16(rO, qoff + 32 * ks, 0));
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s = fmaf((float)ov[e], (float)doreg[ks][e], s);
+      cs[ks] = s;
+    }
+    float half;  // this lane half's chunks (even or odd), in the preprocess kernel's tree
+    if constexpr (D == 128) half = ((cs[0] + cs[4]) + (cs[2] + cs[6])) + ((cs[1] + cs[5]) + (cs[3] + cs[7]));
+    else half = (cs[0] + cs[2]) + (cs[1] + cs[3]);
+    const float full = pair_sum(half);
+    dq_delta = q < N ? full : 0.f;
+  } else {
+    dq_delta = q < N ? Delta[(size_t)bh * N + q] : 0.f;
+  }
   float d_exact = 0.f;  // this lane's share of sum_j P_qj dP_qj
 
   const int kv_end = CAUSAL ? min(N, qt * C::BRQ + C::BRQ) : N;
@@ -648,15 +671,15 @@ hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const floa
 
 template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                       const float* delta, void* dq, float* delta_out, int BH, int N, float scale,
-                       const BlockMask& m, const DropParams& dr, hipStream_t stream) {
+                       const float* delta, const void* o_fused, void* dq, float* delta_out, int BH, int N,
+                       float scale, const BlockMask& m, const DropParams& dr, hipStream_t stream) {
   using C = DqCfg<D>;
   static_assert(C::BRQ == kMaskBlock, "a workgroup owns one block row of the mask");
   const int n_qt = (N + C::BRQ - 1) / C::BRQ;
   const int total = BH * n_qt;
 #define ATTN_DQ_ARGS                                                                                           \
   dim3(total), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, \
-      (bf16*)dq, delta_out, N, n_qt, total, scale * kLog2e, scale
+      (const bf16*)o_fused, (bf16*)dq, delta_out, N, n_qt, total, scale * kLog2e, scale
   if (m.ptr)
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true, false>), ATTN_DQ_ARGS, m.ptr, m.head_stride, m.nb, 0u, 0u, 0u,
                        1.f);
@@ -696,13 +719,15 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const fl
 }
 
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                         const float* delta, void* dq, float* delta_out, int BH, int N, int d, float scale,
-                         bool causal, const BlockMask& m, const DropParams& dr, hipStream_t stream) {
+                         const float* delta, const void* o_fused, void* dq, float* delta_out, int BH, int N, int d,
+                         float scale, bool causal, const BlockMask& m, const DropParams& dr, hipStream_t stream) {
   if (d == 64)
-    return causal ? launch_dq_t<64, true>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, dr, stream)
-                  : launch_dq_t<64, false>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, dr, stream);
-  return causal ? launch_dq_t<128, true>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, dr, stream)
-                : launch_dq_t<128, false>(q, k, v, lse, dout, delta, dq, delta_out, BH, N, scale, m, dr, stream);
+    return causal ? launch_dq_t<64, true>(q, k, v, lse, dout, delta, o_fused, dq, delta_out, BH, N, scale, m, dr, stream)
+                  : launch_dq_t<64, false>(q, k, v, lse, dout, delta, o_fused, dq, delta_out, BH, N, scale, m, dr,
+                                           stream);
+  return causal ? launch_dq_t<128, true>(q, k, v, lse, dout, delta, o_fused, dq, delta_out, BH, N, scale, m, dr, stream)
+                : launch_dq_t<128, false>(q, k, v, lse, dout, delta, o_fused, dq, delta_out, BH, N, scale, m, dr,
+                                          stream);
 }
 
 }  // namespace attn

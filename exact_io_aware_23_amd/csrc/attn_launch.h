@@ -39,10 +39,12 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const fl
                            int d, float scale, bool causal, const BlockMask& mask, const DropParams& drop,
                            hipStream_t stream);
 
+// o_fused != nullptr: the kernel forms delta~ = rowsum(dO * O) itself (bit for
+// bit as launch_bwd_preprocess does) and ignores `delta`.
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
-                         const void* dout, const float* delta, void* dq, float* delta_out, int BH, int N,
-                         int d, float scale, bool causal, const BlockMask& mask, const DropParams& drop,
-                         hipStream_t stream);
+                         const void* dout, const float* delta, const void* o_fused, void* dq, float* delta_out,
+                         int BH, int N, int d, float scale, bool causal, const BlockMask& mask,
+                         const DropParams& drop, hipStream_t stream);
 
 // FP8 forward: q, k, v are e4m3 codes, o bf16; S = scale dq dk Q K^T, O = dv P V.
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,

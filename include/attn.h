@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 typedef enum {
   ATTN_OK = 0,
@@ -69,16 +69,18 @@ attn_status_t attn_fwd(const void* q, const void* k, const void* v, void* o, flo
                        int B, int H, int N, int d, attn_dtype_t dtype, float scale, int causal,
                        void* stream);
 
-/* Bytes of device workspace attn_bwd needs: two fp32 [B,H,N] arrays (the
- * approximate and the exact delta), each B*H*N*4 bytes rounded up to 256.
- * Pure host arithmetic; returns 0 for invalid sizes. */
+/* Bytes of device workspace attn_bwd needs: one fp32 [B,H,N] array (the
+ * exact delta, handed from the dq stage to the dkdv stage), B*H*N*4 bytes
+ * rounded up to 256.  Pure host arithmetic; returns 0 for invalid sizes. */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /* Backward pass: gradients of O with respect to Q, K and V for an upstream
  * gradient dO, given the forward's O and L.  P is recomputed tile by tile from
  * Q, K and L (video page, transcript 06:52-07:24); no N x N array is stored.
- * Enqueues attn_bwd_preprocess, attn_bwd_dq and attn_bwd_dkdv in that order;
- * the dq stage hands the exact delta to the dkdv stage through the workspace.
+ * Enqueues the dq stage and then attn_bwd_dkdv.  The dq stage forms
+ * delta~ = rowsum(dO * O) itself, bit for bit as attn_bwd_preprocess does,
+ * so the result equals preprocess -> attn_bwd_dq -> attn_bwd_dkdv called one
+ * by one; it hands the exact delta to the dkdv stage through the workspace.
  *   q, k, v, o, dout : inputs [B,H,N,d] of `dtype`; lse : input [B,H,N] fp32
  *   dq, dk, dv       : outputs [B,H,N,d] of `dtype`
  *   workspace        : device buffer of at least attn_bwd_workspace_bytes(...)
@@ -122,6 +124,18 @@ attn_status_t attn_bwd_dq(const void* q, const void* k, const void* v, const flo
                           const void* dout, const float* delta, void* dq, float* delta_out, int B,
                           int H, int N, int d, attn_dtype_t dtype, float scale, int causal,
                           void* stream);
+
+/* Backward stages 1 and 2 in one launch, the dq stage that attn_bwd runs: as
+ * attn_bwd_preprocess followed by attn_bwd_dq, bit for bit, but delta~ is
+ * formed from O and dO inside the dq kernel (each workgroup reads the O rows
+ * of its queries once) instead of going through memory.
+ *   q, k, v, o, dout : inputs [B,H,N,d] of `dtype`; lse : fp32 input [B,H,N]
+ *   dq               : output [B,H,N,d] of `dtype`
+ *   delta_out        : output [B,H,N] fp32, the exact delta for attn_bwd_dkdv. */
+attn_status_t attn_bwd_dq_fused(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dout, void* dq, float* delta_out,
+                                int B, int H, int N, int d, attn_dtype_t dtype, float scale,
+                                int causal, void* stream);
 
 /* Block-sparse attention.  The FlashAttention talk transcript
  * (youtube-distilled.com, FThvfkXWqtE), questions after the method part:

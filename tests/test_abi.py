@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess", "attn_bwd_dkdv",
-        "attn_bwd_dq", "attn_status_string", "attn_abi_version", "attn_fwd_block_sparse",
+        "attn_bwd_dq", "attn_bwd_dq_fused", "attn_status_string", "attn_abi_version", "attn_fwd_block_sparse",
         "attn_bwd_block_sparse", "attn_fwd_dropout", "attn_bwd_dropout", "attn_decode_workspace_bytes",
         "attn_decode", "attn_fwd_fp8"])
 
@@ -59,8 +59,8 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.attn_bwd_workspace_bytes(2, 32, 8192, 128) == 2 * (2 * 32 * 8192 * 4)
-    assert lib.attn_bwd_workspace_bytes(1, 1, 3, 64) == 512
+    assert lib.attn_bwd_workspace_bytes(2, 32, 8192, 128) == 2 * 32 * 8192 * 4
+    assert lib.attn_bwd_workspace_bytes(1, 1, 3, 64) == 256
     assert lib.attn_bwd_workspace_bytes(0, 1, 3, 64) == 0
     assert lib.attn_bwd_workspace_bytes(1, 1, -1, 64) == 0
 
@@ -117,6 +117,15 @@ def test_bwd_validation(lib):
     assert lib.attn_bwd_dq(*([FAKE] * 6), None, FAKE, 1, 1, 8, 64, 1, 0.1, 0, None) == INV
     assert lib.attn_bwd_dq(*([FAKE] * 7), None, 1, 1, 8, 64, 1, 0.1, 0, None) == INV
     assert lib.attn_bwd_dq(*([FAKE] * 8), 1, 1, 8, 128, 1, 0.1, 5, None) == INV
+    for i in range(8):
+        p = [FAKE] * 8
+        p[i] = None
+        assert lib.attn_bwd_dq_fused(*p, 1, 1, 8, 64, 1, 0.1, 0, None) == INV, i
+    assert lib.attn_bwd_dq_fused(*([FAKE] * 8), 1, 1, (1 << 22) + 1, 64, 1, 0.1, 0, None) == UNS
+    assert lib.attn_bwd_dq_fused(*([FAKE] * 8), 1, 1, 8, 96, 1, 0.1, 0, None) == UNS
+    assert lib.attn_bwd_dq_fused(*([FAKE] * 8), 1, 1, 8, 64, 0, 0.1, 0, None) == UNS
+    assert lib.attn_bwd_dq_fused(*([FAKE] * 8), 1, 1, 8, 64, 1, 0.0, 0, None) == INV
+    assert lib.attn_bwd_dq_fused(*([FAKE] * 8), 1, 1, 8, 64, 1, 0.1, 2, None) == INV
 
 
 def test_block_sparse_validation(lib):

@@ -249,10 +249,11 @@ def test_workload_n256_d64_short_full(attn):
     check_bf16(f"{w.name} L", got["lse"], l_ref)
 
 
-def test_stage_entry_points_match_attn_bwd(attn):
+@pytest.mark.parametrize("d", [64, 128])
+def test_stage_entry_points_match_attn_bwd(attn, d):
     """preprocess -> dq -> dkdv called one by one equals attn_bwd, and the exact
     delta written by the dq stage equals the oracle's sum_j P_ij dP_ij."""
-    inp = W.draw(2, 2, 777, 64, "bf16", seed=21)
+    inp = W.draw(2, 2, 777, d, "bf16", seed=21)
     scale = 0.125
     q, k, v, do = (inp[x].cuda() for x in ("q", "k", "v", "do"))
     o, lse = attn.fwd(q, k, v, scale=scale, causal=True)
@@ -260,8 +261,11 @@ def test_stage_entry_points_match_attn_bwd(attn):
     delta = attn.bwd_preprocess(o, do)
     dq2, delta_exact = attn.bwd_dq(q, k, v, lse, do, delta, scale=scale, causal=True)
     dk2, dv2 = attn.bwd_dkdv(q, k, v, lse, do, delta_exact, scale=scale, causal=True)
+    # the fused dq stage (what attn_bwd runs) forms delta~ itself, bit for bit
+    dq3, delta_exact3 = attn.bwd_dq_fused(q, k, v, o, lse, do, scale=scale, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    assert torch.equal(dq3, dq2) and torch.equal(delta_exact3, delta_exact)
     qn, kn, vn, don = (inp[x].float().numpy() for x in ("q", "k", "v", "do"))
     for b in range(2):
         for h in range(2):
