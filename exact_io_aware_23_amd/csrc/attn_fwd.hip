@@ -371,6 +371,9 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         pv(par, pop);
         pin_a();
         pin_b();
+        // Without a use here the compiler sinks the row sum's adds past the
+        // mask branch, out of the block where they overlap the MFMAs.
+        asm volatile("" ::"v"(l_run));
         if (needs_mask(kv_a)) mask(nxt, kv_a);
         if (j + 1 < wave_tiles) rescale(tile_max(nxt));
       }
