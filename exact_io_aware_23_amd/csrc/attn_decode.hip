@@ -12,11 +12,15 @@
 // cores.  The work is split over the keys:
 //   * decode_partial_kernel: one workgroup per (batch*head, 512-key chunk).
 //     Four threads per key form the chunk's scores for every query (16-byte
-//     loads of K, partial dot products against q in LDS, two DPP adds); one
-//     wave per query takes the chunk max and exp-sum; then 16 (d=128) or 32
-//     (d=64) key lanes accumulate sum_j p_j V_j with 16-byte loads of V, and
-//     the lanes and waves are reduced through cross-lane swaps and LDS.  The
-//     chunk's (m, l, unnormalised O) go to the workspace.
+//     loads of K kept as bf16 pairs, v_dot2_f32_bf16 against q held in LDS as
+//     bf16 pairs, two DPP adds); one wave per query takes the chunk max and
+//     exp-sum; then 16 (d=128) or 32 (d=64) key lanes accumulate
+//     sum_j p_j V_j two keys at a time: the two V rows are interleaved into
+//     bf16 pairs, p of both keys is rounded to one bf16 pair (as the forward
+//     rounds P before its P V product; l sums the unrounded p), and one
+//     v_dot2_f32_bf16 adds both keys' products to a column.  The lanes and
+//     waves are reduced through cross-lane swaps and LDS.  The chunk's
+//     (m, l, unnormalised O) go to the workspace.
 //   * decode_merge_kernel: per (batch*head, query) it merges the chunks with
 //     the online-softmax rule of the same page (04:46-05:17): m = max m_c,
 //     l = sum 2^(m_c - m) l_c, O = sum 2^(m_c - m) O_c / l.
@@ -45,7 +49,7 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
   constexpr int G8 = D / 8;          // 8-dim groups in pass 2
   constexpr int KL = 256 / G8;       // key lanes in pass 2
   static_assert(NQ >= 1 && NQ <= kDecMaxQ, "query capacity");
-  __shared__ __attribute__((aligned(16))) float qs[NQ][D];
+  __shared__ __attribute__((aligned(16))) uint32_t qs2[NQ][D / 2];  // q as packed bf16 pairs
   __shared__ float sc[NQ][kDecChunk];
   __shared__ __attribute__((aligned(16))) float red[4][NQ][D];
 
@@ -59,7 +63,10 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
   const rsrc_t rK = make_rsrc(K + (size_t)bh * Nk * D, head_bytes);
   const rsrc_t rV = make_rsrc(V + (size_t)bh * Nk * D, head_bytes);
 
-  for (int idx = tid; idx < nq * D; idx += 256) qs[idx / D][idx % D] = (float)Q[(size_t)bh * nq * D + idx];
+  {
+    const uint32_t* q2 = reinterpret_cast<const uint32_t*>(Q + (size_t)bh * nq * D);
+    for (int idx = tid; idx < nq * D / 2; idx += 256) qs2[idx / (D / 2)][idx % (D / 2)] = q2[idx];
+  }
   __syncthreads();
 
   // ---- pass 1: scores of the chunk, in base-2 units; masked keys get -inf
@@ -68,25 +75,26 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
 #pragma unroll 2
     for (int kt = 0; kt < kDecChunk; kt += kDecTile) {
       const int key = k0 + kt + kl;
-      float kv[DP];
+      // K stays packed: v_dot2_f32_bf16 takes two bf16 products per
+      // instruction (each exact in fp32) and q comes from LDS as bf16 pairs
+      u32x4 kw[DP / 8];
 #pragma unroll
-      for (int i = 0; i < DP / 8; ++i) {
-        const u32x4 raw = bload16(rK, (key * D + part * DP + 8 * i) * 2, 0);
-        const bf16x8 b = __builtin_bit_cast(bf16x8, raw);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kv[8 * i + e] = (float)b[e];
-      }
+      for (int i = 0; i < DP / 8; ++i) kw[i] = bload16(rK, (key * D + part * DP + 8 * i) * 2, 0);
 #pragma unroll
       for (int qi = 0; qi < NQ; ++qi) {
         if (qi >= nq) break;
         float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < DP; e += 4) {
-          const f32x4 qv = *reinterpret_cast<const f32x4*>(&qs[qi][part * DP + e]);
-          acc = fmaf(kv[e], qv[0], acc);
-          acc = fmaf(kv[e + 1], qv[1], acc);
-          acc = fmaf(kv[e + 2], qv[2], acc);
-          acc = fmaf(kv[e + 3], qv[3], acc);
+        for (int i = 0; i < DP / 8; ++i) {
+          const u32x4 qv = *reinterpret_cast<const u32x4*>(&qs2[qi][(part * DP + 8 * i) / 2]);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            // (vector elements go through plain words: a bit_cast of a
+            // subscripted vector element read element 0 with this compiler)
+            const uint32_t kx = kw[i][w], qx = qv[w];
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kx), __builtin_bit_cast(bf16x2, qx), acc,
+                                                  false);
+          }
         }
         acc += __builtin_bit_cast(float, quad_xor<1>(__builtin_bit_cast(uint32_t, acc)));
         acc += __builtin_bit_cast(float, quad_xor<2>(__builtin_bit_cast(uint32_t, acc)));
@@ -125,18 +133,26 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
   for (int qi = 0; qi < NQ; ++qi)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[qi][e] = 0.f;
-#pragma unroll 4
-  for (int kj = kl2; kj < kDecChunk; kj += KL) {
-    const bf16x8 b = __builtin_bit_cast(bf16x8, bload16(rV, ((k0 + kj) * D + 8 * g8) * 2, 0));
-    float vv[8];
+  // two keys per step: V rows kj and kj + KL are interleaved into bf16 pairs
+  // (one v_perm per pair) and p of both keys is rounded to one bf16 pair, so
+  // each v_dot2_f32_bf16 adds two keys' products to a column
+#pragma unroll 2
+  for (int kj = kl2; kj < kDecChunk; kj += 2 * KL) {
+    const u32x4 va = bload16(rV, ((k0 + kj) * D + 8 * g8) * 2, 0);
+    const u32x4 vb = bload16(rV, ((k0 + kj + KL) * D + 8 * g8) * 2, 0);
+    uint32_t pr[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vv[e] = (float)b[e];
+    for (int w = 0; w < 4; ++w) {
+      pr[2 * w] = __builtin_amdgcn_perm(vb[w], va[w], 0x05040100u);      // element 2w of both keys
+      pr[2 * w + 1] = __builtin_amdgcn_perm(vb[w], va[w], 0x07060302u);  // element 2w + 1
+    }
 #pragma unroll
     for (int qi = 0; qi < NQ; ++qi) {
       if (qi >= nq) break;
-      const float p = sc[qi][kj];
+      const bf16x2 pp = __builtin_bit_cast(bf16x2, pack_bf16x2(sc[qi][kj], sc[qi][kj + KL]));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[qi][e] = fmaf(p, vv[e], acc[qi][e]);
+      for (int e = 0; e < 8; ++e)
+        acc[qi][e] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pr[e]), pp, acc[qi][e], false);
     }
   }
   // lanes of one wave with the same g8 hold different keys: fold them
