@@ -515,7 +515,7 @@ def bench_fp8(args, w):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(every (batch, head) pair is independent, so N GPUs would each run B*H/N heads).", file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
