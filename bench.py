@@ -122,8 +122,9 @@ def timed_oracle(run_head, per_head: float, unit: str, budget_s: float, what: st
             "sample": f"{heads} head(s): {what}, {dt:.1f} s; the rate counts the same algorithmic work as value"}
 
 
-def cpu_baseline(w: W.Workload, budget_s: float):
-    """Time the fp64 oracle (forward + backward) head by head for about budget_s."""
+def cpu_baseline(w: W.Workload, budget_s: float, fwd_only: bool = False):
+    """Time the fp64 oracle head by head for about budget_s: forward + backward,
+    or the forward alone when the GPU line times the forward alone."""
     import numpy as np
     from oracle import attention as orc
 
@@ -132,10 +133,13 @@ def cpu_baseline(w: W.Workload, budget_s: float):
 
     def head():
         orc.forward_head(q, k, v, w.scale, w.causal)
-        orc.backward_head(q, k, v, do, w.scale, w.causal)
+        if not fwd_only:
+            orc.backward_head(q, k, v, do, w.scale, w.causal)
 
-    return timed_oracle(head, (w.fwd_flops() + w.bwd_flops()) / (w.B * w.H), "TFLOP/s", budget_s,
-                        f"the workload (N={w.N}, d={w.d}, causal={w.causal}), forward + backward in fp64 with S "
+    flops = w.fwd_flops() + (0.0 if fwd_only else w.bwd_flops())
+    what = "forward" if fwd_only else "forward + backward"
+    return timed_oracle(head, flops / (w.B * w.H), "TFLOP/s", budget_s,
+                        f"the workload (N={w.N}, d={w.d}, causal={w.causal}), {what} in fp64 with S "
                         "and P materialised")
 
 
@@ -639,7 +643,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, fwd_only)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -415,32 +415,36 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 
 // ---------------------------------------------------------------------------
 // fp32 forward: the same online-softmax algorithm on plain fp32 VALU
-// arithmetic.  One thread owns one query row (q and the O accumulator in
-// VGPRs); 32-key K/V tiles are staged in LDS and read as broadcasts.
+// arithmetic.  Four threads share a query row, each holding a quarter of its
+// d columns of q and of the O accumulator; a score is their four partial dot
+// products joined by two lane swaps, so all four hold the same scores, max
+// and sum.  32-key K/V tiles are staged in LDS and read as broadcasts.
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
 fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                float* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, float c) {
   constexpr int BC = 32;
+  constexpr int DP = D / 4;  // columns per thread
   __shared__ float Ks[BC][D];
   __shared__ float Vs[BC][D];
   const int bh = blockIdx.x / n_qtiles;
   const int qt = blockIdx.x % n_qtiles;
   const size_t head = (size_t)bh * N * D;
-  const int q = qt * 64 + threadIdx.x;
+  const int d0 = (threadIdx.x & 3) * DP;
+  const int q = qt * 64 + (threadIdx.x >> 2);
   const bool qv = q < N;
 
-  float qr[D], acc[D];
+  float qr[DP], acc[DP];
 #pragma unroll
-  for (int i = 0; i < D; ++i) {
-    qr[i] = qv ? Q[head + (size_t)q * D + i] : 0.f;
+  for (int i = 0; i < DP; ++i) {
+    qr[i] = qv ? Q[head + (size_t)q * D + d0 + i] : 0.f;
     acc[i] = 0.f;
   }
   float m_run = -1e30f, l_run = 0.f;
   const int kv_end = CAUSAL ? min(N, qt * 64 + 64) : N;
   for (int kv0 = 0; kv0 < kv_end; kv0 += BC) {
     __syncthreads();
-    for (int idx = threadIdx.x; idx < BC * D; idx += 64) {
+    for (int idx = threadIdx.x; idx < BC * D; idx += 256) {
       const int row = idx / D, col = idx % D;
       const int key = kv0 + row;
       Ks[row][col] = key < N ? K[head + (size_t)key * D + col] : 0.f;
@@ -453,7 +457,9 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
     for (int j = 0; j < BC; ++j) {
       float dot = 0.f;
 #pragma unroll
-      for (int i = 0; i < D; ++i) dot = fmaf(qr[i], Ks[j][i], dot);
+      for (int i = 0; i < DP; ++i) dot = fmaf(qr[i], Ks[j][d0 + i], dot);
+      dot += __shfl_xor(dot, 1);
+      dot += __shfl_xor(dot, 2);
       const int key = kv0 + j;
       const bool bad = key >= N || (CAUSAL && key > q);
       s[j] = bad ? -INFINITY : dot;
@@ -464,21 +470,21 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
     m_run = m_new;
     float rs = 0.f;
 #pragma unroll
-    for (int i = 0; i < D; ++i) acc[i] *= alpha;
+    for (int i = 0; i < DP; ++i) acc[i] *= alpha;
 #pragma unroll
     for (int j = 0; j < BC; ++j) {
       const float p = exp2f(fmaf(s[j], c, -m_new));
       rs += p;
 #pragma unroll
-      for (int i = 0; i < D; ++i) acc[i] = fmaf(p, Vs[j][i], acc[i]);
+      for (int i = 0; i < DP; ++i) acc[i] = fmaf(p, Vs[j][d0 + i], acc[i]);
     }
     l_run = l_run * alpha + rs;
   }
   if (qv) {
     const float inv = 1.0f / l_run;
 #pragma unroll
-    for (int i = 0; i < D; ++i) O[head + (size_t)q * D + i] = acc[i] * inv;
-    L[(size_t)bh * N + q] = (m_run + log2f(l_run)) * kLn2;
+    for (int i = 0; i < DP; ++i) O[head + (size_t)q * D + d0 + i] = acc[i] * inv;
+    if (d0 == 0) L[(size_t)bh * N + q] = (m_run + log2f(l_run)) * kLn2;
   }
 }
 
@@ -517,7 +523,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_fwd_f32_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                             int N, float scale, hipStream_t stream) {
   const int n_qtiles = (N + 63) / 64;
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(BH * n_qtiles), dim3(64), 0, stream,
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(BH * n_qtiles), dim3(256), 0, stream,
                      (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, N, n_qtiles,
                      scale * kLog2e);
   return hipGetLastError();
