@@ -119,7 +119,8 @@ def timed_oracle(run_head, per_head: float, unit: str, budget_s: float, what: st
     dt = time.perf_counter() - t0
     div = 1e12 if unit == "TFLOP/s" else 1e9
     return {"value": per_head * heads / dt / div, "unit": unit, "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads} head(s): {what}, {dt:.1f} s; the rate counts the same algorithmic work as value"}
+            "sample": f"{heads} head(s): {what}, {dt:.1f} s; the rate counts the same algorithmic work as value",
+            "cores_note": "BLAS threads the oracle's numpy matrix products used", **host_facts()}
 
 
 def cpu_baseline(w: W.Workload, budget_s: float, fwd_only: bool = False):
@@ -141,6 +142,98 @@ def cpu_baseline(w: W.Workload, budget_s: float, fwd_only: bool = False):
     return timed_oracle(head, flops / (w.B * w.H), "TFLOP/s", budget_s,
                         f"the workload (N={w.N}, d={w.d}, causal={w.causal}), {what} in fp64 with S "
                         "and P materialised")
+
+
+def host_facts():
+    """The host the oracle ran on: CPU model, logical CPUs and the affinity set."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (amdsmi GPU metrics: the per-XCD current
+    gfx clocks, else the current or average gfx clock, in MHz) from a thread
+    every `period` seconds while active.  The GPU is matched to torch's device
+    0 by PCI bus.  mean() is None, with `error` set, when the metrics cannot be
+    read on this host."""
+
+    def __init__(self, period: float = 0.002):
+        import threading
+
+        self.period, self.samples, self.error = period, [], None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+
+            self._smi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                if bus is None or int(bdf.split(":")[1], 16) == int(bus):
+                    self._handle = h
+                    break
+            if self._handle is None:
+                self.error = f"no amdsmi device on PCI bus {bus}"
+        except Exception as e:  # pragma: no cover - depends on the host
+            self.error = f"amdsmi unavailable: {type(e).__name__}: {e}"
+
+    def _read(self):
+        m = self._smi.amdsmi_get_gpu_metrics_info(self._handle)
+        vals = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 65535]
+        if vals:
+            return sum(vals) / len(vals)
+        for key in ("current_gfxclk", "average_gfxclk_frequency"):
+            x = m.get(key)
+            if isinstance(x, (int, float)) and 0 < x < 65535:
+                return float(x)
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                x = self._read()
+                if x is not None:
+                    self.samples.append(x)
+            except Exception as e:  # pragma: no cover
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+
+        if self._handle is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        return False
+
+    def mean(self):
+        return sum(self.samples) / len(self.samples) if self.samples else None
+
+    def report(self):
+        m = self.mean()
+        return {"gpu_clock_mhz_avg": round(m, 1) if m is not None else None, "gpu_clock_samples": len(self.samples),
+                "gpu_clock_source": "amdsmi gpu metrics (per-XCD current gfx clock), sampled every "
+                                    f"{self.period * 1e3:.0f} ms during the timed steps"
+                                    + (f"; {self.error}" if self.error else "")}
 
 
 COPY_BYTES = 1 << 30
@@ -580,12 +673,14 @@ def main():
     torch.cuda.synchronize()
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    clock = ClockSampler()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with clock:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(events[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     samples = {n: [ev[j].elapsed_time(ev[j + 1]) for ev in events] for j, n in enumerate(names)}
     per_kernel = {n: sum(t) / args.steps for n, t in samples.items()}  # ms per launch
@@ -641,7 +736,11 @@ def main():
         "kernel_ms_median": {n: round(sorted(t)[len(t) // 2], 4) for n, t in samples.items()},
         "kernel_ms_min": {n: round(min(t), 4) for n, t in samples.items()},
         "roofline": roof,
+        "host": {**host_facts(), **clock.report()},
     }
+    if clock.mean() is not None:
+        # the MFMA peak at the clock the kernels actually ran at, for context
+        out["mfma_peak_at_measured_clock_tflops"] = round(MFMA_BF16_PEAK_TFLOPS * clock.mean() / 2400.0, 1)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, fwd_only)
     print(json.dumps(out), flush=True)

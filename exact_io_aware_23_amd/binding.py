@@ -296,7 +296,8 @@ def decode(q, k_cache, v_cache, scale: float | None = None, causal: bool = False
 def bwd_preprocess(o, do, delta=None):
     """attn_bwd_preprocess; returns delta fp32 [B, H, N]."""
     B, H, N, d = o.shape
-    _check("do", do, (B, H, N, d), o.dtype)
+    for name, t in (("o", o), ("do", do)):
+        _check(name, t, (B, H, N, d), o.dtype)
     delta = torch.empty((B, H, N), dtype=torch.float32, device=o.device) if delta is None else delta
     _check("delta", delta, (B, H, N), torch.float32)
     _call("attn_bwd_preprocess", o.data_ptr(), do.data_ptr(), delta.data_ptr(), B, H, N, d, _dtype_code(o),
@@ -309,7 +310,7 @@ def bwd_dkdv(q, k, v, lse, do, delta, scale: float | None = None, causal: bool =
     B, H, N, d = q.shape
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for name, t in (("k", k), ("v", v), ("do", do), ("dk", dk), ("dv", dv)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do), ("dk", dk), ("dv", dv)):
         _check(name, t, (B, H, N, d), q.dtype)
     _check("lse", lse, (B, H, N), torch.float32)
     _check("delta", delta, (B, H, N), torch.float32)
@@ -325,7 +326,7 @@ def bwd_dq(q, k, v, lse, do, delta, scale: float | None = None, causal: bool = F
     B, H, N, d = q.shape
     dq = torch.empty_like(q) if dq is None else dq
     delta_out = torch.empty_like(delta) if delta_out is None else delta_out
-    for name, t in (("k", k), ("v", v), ("do", do), ("dq", dq)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("do", do), ("dq", dq)):
         _check(name, t, (B, H, N, d), q.dtype)
     _check("lse", lse, (B, H, N), torch.float32)
     _check("delta", delta, (B, H, N), torch.float32)
@@ -341,7 +342,7 @@ def bwd_dq_fused(q, k, v, o, lse, do, scale: float | None = None, causal: bool =
     B, H, N, d = q.shape
     dq = torch.empty_like(q) if dq is None else dq
     delta_out = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta_out is None else delta_out
-    for name, t in (("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq)):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq)):
         _check(name, t, (B, H, N, d), q.dtype)
     _check("lse", lse, (B, H, N), torch.float32)
     _check("delta_out", delta_out, (B, H, N), torch.float32)

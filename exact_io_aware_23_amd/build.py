@@ -15,6 +15,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_fwd_fp8.hip"]
+# per-file extra flags (none at present)
+EXTRA_FLAGS: dict = {}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -30,14 +32,18 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str | None = None, build_dir: str | None = None,
+          defines: tuple = ()) -> str:
+    """Compile every source and link the library (to `out`, default libattn.so)."""
+    bdir = build_dir or BUILD_DIR
+    lib_path = out or LIB_PATH
+    os.makedirs(bdir, exist_ok=True)
     procs = []
     objs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), *defines, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
@@ -53,13 +59,13 @@ def build(verbose: bool = False) -> str:
         for src, out in failed:
             sys.stderr.write(f"hipcc failed for {src}:\n{out}\n")
         raise RuntimeError("HIP build failed: " + ", ".join(s for s, _ in failed))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -15,7 +15,10 @@ bool sizes_ok(int B, int H, int N) {
   return rows < ((int64_t)1 << 31);
 }
 
-bool scale_ok(float scale) { return std::isfinite(scale) && scale > 0.f; }
+// any finite scale: the kernels run the softmax with |scale| and apply its
+// sign (or zero) to the operand they hold in registers
+bool scale_ok(float scale) { return std::isfinite(scale); }
+bool descale_ok(float x) { return std::isfinite(x) && x > 0.f; }
 
 // the kernels address one (batch, head) slab with 32-bit byte offsets
 constexpr int kMaxN = 1 << 22;
@@ -249,9 +252,10 @@ attn_status_t attn_fwd_fp8(const void* q, const void* k, const void* v, float de
                            int causal, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID;
   if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
-  if (!scale_ok(descale_q) || !scale_ok(descale_k) || !scale_ok(descale_v)) return ATTN_ERR_INVALID;
-  const float c = (float)((double)scale * descale_q * descale_k);
-  if (!scale_ok(c)) return ATTN_ERR_INVALID;
+  if (!descale_ok(descale_q) || !descale_ok(descale_k) || !descale_ok(descale_v)) return ATTN_ERR_INVALID;
+  // |scale dq dk| must be a finite fp32 value, and not round to 0 unless scale is 0
+  const float c = (float)((double)(scale < 0.f ? -scale : scale) * descale_q * descale_k);
+  if (!std::isfinite(c) || (scale != 0.f && c == 0.f)) return ATTN_ERR_INVALID;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
   return map_hip(attn::launch_fwd_fp8(q, k, v, o, lse, B * H, N, d, scale, descale_q, descale_k, descale_v,

@@ -124,7 +124,7 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
                 const float* __restrict__ Lse, const bf16* __restrict__ dO, const float* __restrict__ Delta,
                 bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int n_ktiles, int total, float c,
                 float scale, const uint8_t* __restrict__ Mask, int mask_hs, int nb, uint32_t drop_t,
-                uint32_t seed_lo, uint32_t seed_hi, float inv_keep) {
+                uint32_t seed_lo, uint32_t seed_hi, float inv_keep, uint32_t smode) {
   using C = DkdvCfg<D>;
   static_assert(!(SPARSE && DROP), "block-sparse and dropout are separate entry points");
   __shared__ __attribute__((aligned(16))) char smem[C::BYTES];
@@ -160,7 +160,7 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   bf16x8 kreg[C::KS];
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks)
-    kreg[ks] = __builtin_bit_cast(bf16x8, bload16(rK, (key * D + 16 * ks + 8 * g) * 2, 0));
+    kreg[ks] = sign_bf16x8(__builtin_bit_cast(bf16x8, bload16(rK, (key * D + 16 * ks + 8 * g) * 2, 0)), smode);
   // buffer -> LDS copies: 1 KB block b of a [rows][D] tile gets 16-byte chunk
   // idx = 64 b + lane, stored at its swizzled position
   auto tile_off = [&](int b) {
@@ -417,7 +417,7 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
               const float* __restrict__ Lse, const bf16* __restrict__ dO, const float* __restrict__ Delta,
               const bf16* __restrict__ Ofused, bf16* __restrict__ dQ, float* __restrict__ DeltaOut, int N, int n_qtiles, int total, float c,
               float scale, const uint8_t* __restrict__ Mask, int mask_hs, int nb, uint32_t drop_t,
-              uint32_t seed_lo, uint32_t seed_hi, float inv_keep) {
+              uint32_t seed_lo, uint32_t seed_hi, float inv_keep, uint32_t smode) {
   using C = DqCfg<D>;
   static_assert(!(SPARSE && DROP), "block-sparse and dropout are separate entry points");
   // one array per stage: the compiler then knows that reads of one stage do
@@ -453,7 +453,7 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
   const int qoff = (q * D + 8 * g) * 2;
 #pragma unroll
   for (int ks = 0; ks < C::KS; ++ks) {
-    qreg[ks] = __builtin_bit_cast(bf16x8, bload16(rQ, qoff + 32 * ks, 0));
+    qreg[ks] = sign_bf16x8(__builtin_bit_cast(bf16x8, bload16(rQ, qoff + 32 * ks, 0)), smode);
     doreg[ks] = __builtin_bit_cast(bf16x8, bload16(rdO, qoff + 32 * ks, 0));
   }
   // rows past N, and rows with no allowed key (L = -inf), get p = exp2(-inf) = 0
@@ -653,18 +653,19 @@ hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const floa
   static_assert(C::BKV == kMaskBlock, "a workgroup owns one block column of the mask");
   const int n_kt = (N + C::BKV - 1) / C::BKV;
   const int total = BH * n_kt;
+  const ScoreScale sc = split_scale(scale);
 #define ATTN_DKDV_ARGS                                                                                         \
   dim3(total), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, \
-      (bf16*)dk, (bf16*)dv, N, n_kt, total, scale * kLog2e, scale
+      (bf16*)dk, (bf16*)dv, N, n_kt, total, sc.c, scale
   if (m.ptr)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true, false>), ATTN_DKDV_ARGS, m.ptr, m.head_stride, m.nb, 0u, 0u,
-                       0u, 1.f);
+                       0u, 1.f, sc.mode);
   else if (dr.on)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false, true>), ATTN_DKDV_ARGS, (const uint8_t*)nullptr, 0, 0,
-                       dr.t, dr.seed_lo, dr.seed_hi, dr.inv_keep);
+                       dr.t, dr.seed_lo, dr.seed_hi, dr.inv_keep, sc.mode);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false, false>), ATTN_DKDV_ARGS, (const uint8_t*)nullptr, 0, 0,
-                       0u, 0u, 0u, 1.f);
+                       0u, 0u, 0u, 1.f, sc.mode);
 #undef ATTN_DKDV_ARGS
   return hipGetLastError();
 }
@@ -677,18 +678,19 @@ hipError_t launch_dq_t(const void* q, const void* k, const void* v, const float*
   static_assert(C::BRQ == kMaskBlock, "a workgroup owns one block row of the mask");
   const int n_qt = (N + C::BRQ - 1) / C::BRQ;
   const int total = BH * n_qt;
+  const ScoreScale sc = split_scale(scale);
 #define ATTN_DQ_ARGS                                                                                           \
   dim3(total), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, \
-      (const bf16*)o_fused, (bf16*)dq, delta_out, N, n_qt, total, scale * kLog2e, scale
+      (const bf16*)o_fused, (bf16*)dq, delta_out, N, n_qt, total, sc.c, scale
   if (m.ptr)
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, true, false>), ATTN_DQ_ARGS, m.ptr, m.head_stride, m.nb, 0u, 0u, 0u,
-                       1.f);
+                       1.f, sc.mode);
   else if (dr.on)
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, true>), ATTN_DQ_ARGS, (const uint8_t*)nullptr, 0, 0, dr.t,
-                       dr.seed_lo, dr.seed_hi, dr.inv_keep);
+                       dr.seed_lo, dr.seed_hi, dr.inv_keep, sc.mode);
   else
     hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, false, false>), ATTN_DQ_ARGS, (const uint8_t*)nullptr, 0, 0, 0u, 0u,
-                       0u, 1.f);
+                       0u, 1.f, sc.mode);
 #undef ATTN_DQ_ARGS
   return hipGetLastError();
 }

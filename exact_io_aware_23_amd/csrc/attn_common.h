@@ -152,6 +152,56 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);  // [a.hi, b.hi]
 }
 
+// Sign of the score scale.  The tiled kernels take a tile's max over the
+// unscaled scores and fold c = scale * log2(e) into the exponent FMA, which
+// needs c > 0.  A negative or zero scale is applied to the operand a kernel
+// holds in registers instead (Q, or K in the key-stationary backward), and
+// the kernel runs with c = |scale| log2(e) (log2(e) itself when scale = 0):
+//   kSignNeg : the operand's sign bits are flipped (exact), so every score
+//              changes sign and |scale| s = scale (q . k);
+//   kSignZero: every finite element becomes +0 and every non-finite one NaN,
+//              so each score is 0 * (q . k): 0, or NaN where q . k is not finite.
+// Products that multiply by the scale itself (dQ, dK) use the signed scale.
+enum : uint32_t { kSignPos = 0, kSignNeg = 1, kSignZero = 2 };
+
+// one dword of two packed bf16 values
+__device__ __forceinline__ uint32_t sign_word_bf16(uint32_t u, uint32_t mode) {
+  if (mode == kSignNeg) return u ^ 0x80008000u;
+  if (mode == kSignZero) {
+    const uint32_t lo = (u & 0x7F80u) == 0x7F80u ? 0x7FC0u : 0u;
+    const uint32_t hi = (u & 0x7F800000u) == 0x7F800000u ? 0x7FC00000u : 0u;
+    return lo | hi;
+  }
+  return u;
+}
+__device__ __forceinline__ bf16x8 sign_bf16x8(const bf16x8& v, uint32_t mode) {
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+  u32x4 r;
+  r[0] = sign_word_bf16(u[0], mode);
+  r[1] = sign_word_bf16(u[1], mode);
+  r[2] = sign_word_bf16(u[2], mode);
+  r[3] = sign_word_bf16(u[3], mode);
+  return __builtin_bit_cast(bf16x8, r);
+}
+// one fp32 element
+__device__ __forceinline__ float sign_f32(float x, uint32_t mode) {
+  if (mode == kSignNeg) return -x;
+  if (mode == kSignZero) return __builtin_isfinite(x) ? 0.f : __builtin_nanf("");
+  return x;
+}
+// one dword of four OCP e4m3 codes (S.1111.111 is NaN; there is no infinity)
+__device__ __forceinline__ uint32_t sign_word_e4m3(uint32_t u, uint32_t mode) {
+  if (mode == kSignNeg) return u ^ 0x80808080u;
+  if (mode == kSignZero) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (((u >> (8 * b)) & 0x7Fu) == 0x7Fu) r |= 0x7Fu << (8 * b);
+    return r;
+  }
+  return u;
+}
+
 // XCD-aware work index.  Workgroups are handed to the 8 XCDs round-robin by
 // linear id; renumbering so that each XCD walks a contiguous range of work
 // items keeps the tiles of one head (which share K/V, or Q/dO) in one L2.

@@ -76,7 +76,7 @@ __global__ void __launch_bounds__(256, PIPE ? 2 : 4)
 fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                 bf16* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, int total, float c,
                 const uint8_t* __restrict__ Mask, int mask_hs, int nb, uint32_t drop_t, uint32_t seed_lo,
-                uint32_t seed_hi, float inv_keep) {
+                uint32_t seed_hi, float inv_keep, uint32_t smode) {
   using C = FwdCfg<D>;
   static_assert(!(SPARSE && DROP), "block-sparse and dropout are separate entry points");
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
@@ -114,6 +114,10 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     const int qoff = (q * D + 8 * g) * 2;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, bload16(rQ, qoff + 32 * ks, 0));
+    if (smode != kSignPos) {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) qreg[ks] = sign_bf16x8(qreg[ks], smode);
+    }
   }
   if constexpr (SPARSE) {
     // (after the Q loads are issued, so the two latencies overlap)
@@ -422,7 +426,7 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256)
 fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-               float* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, float c) {
+               float* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, float c, uint32_t smode) {
   constexpr int BC = 32;
   constexpr int DP = D / 4;  // columns per thread
   __shared__ float Ks[BC][D];
@@ -437,7 +441,7 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
   float qr[DP], acc[DP];
 #pragma unroll
   for (int i = 0; i < DP; ++i) {
-    qr[i] = qv ? Q[head + (size_t)q * D + d0 + i] : 0.f;
+    qr[i] = sign_f32(qv ? Q[head + (size_t)q * D + d0 + i] : 0.f, smode);
     acc[i] = 0.f;
   }
   float m_run = -1e30f, l_run = 0.f;
@@ -500,22 +504,23 @@ hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* 
   // workgroups by LDS as well as registers)
   constexpr bool kShortFwd = D == 64;
   const bool short_seq = kShortFwd && N <= kShortSeqMaxN;
+  const ScoreScale sc = split_scale(scale);
   if (m.ptr)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, false>), dim3(total), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
-                       scale * kLog2e, m.ptr, m.head_stride, m.nb, 0u, 0u, 0u, 1.f);
+                       sc.c, m.ptr, m.head_stride, m.nb, 0u, 0u, 0u, 1.f, sc.mode);
   else if (dr.on)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, true>), dim3(total), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
-                       scale * kLog2e, (const uint8_t*)nullptr, 0, 0, dr.t, dr.seed_lo, dr.seed_hi, dr.inv_keep);
+                       sc.c, (const uint8_t*)nullptr, 0, 0, dr.t, dr.seed_lo, dr.seed_hi, dr.inv_keep, sc.mode);
   else if (short_seq)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, false, /*PIPE=*/!kShortFwd>), dim3(total), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
-                       scale * kLog2e, (const uint8_t*)nullptr, 0, 0, 0u, 0u, 0u, 1.f);
+                       sc.c, (const uint8_t*)nullptr, 0, 0, 0u, 0u, 0u, 1.f, sc.mode);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, false>), dim3(total), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
-                       scale * kLog2e, (const uint8_t*)nullptr, 0, 0, 0u, 0u, 0u, 1.f);
+                       sc.c, (const uint8_t*)nullptr, 0, 0, 0u, 0u, 0u, 1.f, sc.mode);
   return hipGetLastError();
 }
 
@@ -523,9 +528,10 @@ template <int D, bool CAUSAL>
 hipError_t launch_fwd_f32_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                             int N, float scale, hipStream_t stream) {
   const int n_qtiles = (N + 63) / 64;
+  const ScoreScale sc = split_scale(scale);
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(BH * n_qtiles), dim3(256), 0, stream,
-                     (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, N, n_qtiles,
-                     scale * kLog2e);
+                     (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, N, n_qtiles, sc.c,
+                     sc.mode);
   return hipGetLastError();
 }
 

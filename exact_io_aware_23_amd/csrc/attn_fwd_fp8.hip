@@ -92,7 +92,7 @@ template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
 fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
                bf16* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, int total, float c,
-               float dv) {
+               float dv, uint32_t smode) {
   using C = Fp8Cfg<D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
 
@@ -127,6 +127,10 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
     const i32x4 lo = __builtin_bit_cast(i32x4, bload16(rQ, off, 0));
     const i32x4 hi = __builtin_bit_cast(i32x4, bload16(rQ, off + 16, 0));
     qreg[ks] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    if (smode != kSignPos) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qreg[ks][e] = (int)sign_word_e4m3((uint32_t)qreg[ks][e], smode);
+    }
   }
 
   // ---- buffer -> LDS copies: wave `wave`, copy i fills 1 KB block
@@ -364,12 +368,12 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
 
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_fp8_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                            float c, float dv, hipStream_t stream) {
+                            float c, float dv, uint32_t smode, hipStream_t stream) {
   using C = Fp8Cfg<D>;
   const int n_qtiles = (N + C::BR - 1) / C::BR;
   const int total = BH * n_qtiles;
   hipLaunchKernelGGL((fwd_fp8_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, stream, (const uint8_t*)q,
-                     (const uint8_t*)k, (const uint8_t*)v, (bf16*)o, lse, N, n_qtiles, total, c, dv);
+                     (const uint8_t*)k, (const uint8_t*)v, (bf16*)o, lse, N, n_qtiles, total, c, dv, smode);
   return hipGetLastError();
 }
 
@@ -377,11 +381,14 @@ hipError_t launch_fwd_fp8_t(const void* q, const void* k, const void* v, void* o
 
 hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
                           float scale, float dq, float dk, float dv, bool causal, hipStream_t stream) {
-  const float c = (float)((double)scale * dq * dk * 1.4426950408889634);
-  if (d == 64) return causal ? launch_fwd_fp8_t<64, true>(q, k, v, o, lse, BH, N, c, dv, stream)
-                             : launch_fwd_fp8_t<64, false>(q, k, v, o, lse, BH, N, c, dv, stream);
-  return causal ? launch_fwd_fp8_t<128, true>(q, k, v, o, lse, BH, N, c, dv, stream)
-                : launch_fwd_fp8_t<128, false>(q, k, v, o, lse, BH, N, c, dv, stream);
+  // the exponent factor |scale dq dk| log2 e; the sign of scale goes into Q (kSignNeg / kSignZero)
+  const uint32_t mode = scale > 0.f ? kSignPos : scale < 0.f ? kSignNeg : kSignZero;
+  const double mag = scale == 0.f ? 1.0 : (double)(scale < 0.f ? -scale : scale) * dq * dk;
+  const float c = (float)(mag * 1.4426950408889634);
+  if (d == 64) return causal ? launch_fwd_fp8_t<64, true>(q, k, v, o, lse, BH, N, c, dv, mode, stream)
+                             : launch_fwd_fp8_t<64, false>(q, k, v, o, lse, BH, N, c, dv, mode, stream);
+  return causal ? launch_fwd_fp8_t<128, true>(q, k, v, o, lse, BH, N, c, dv, mode, stream)
+                : launch_fwd_fp8_t<128, false>(q, k, v, o, lse, BH, N, c, dv, mode, stream);
 }
 
 }  // namespace attn

@@ -27,6 +27,20 @@ struct DropParams {
   float inv_keep = 1.f;
 };
 
+// The factor the kernels fold into their exponent FMA (c = |scale| log2 e,
+// or log2 e when scale = 0) and how the sign of scale is applied to the
+// operand held in registers (kSignPos / kSignNeg / kSignZero of attn_common.h).
+struct ScoreScale {
+  float c;
+  uint32_t mode;
+};
+inline ScoreScale split_scale(float scale) {
+  constexpr float kLog2eHost = 1.4426950408889634f;
+  if (scale > 0.f) return {scale * kLog2eHost, 0u};
+  if (scale < 0.f) return {-scale * kLog2eHost, 1u};
+  return {kLog2eHost, 2u};
+}
+
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
                       int d, bool bf16_in, float scale, bool causal, const BlockMask& mask, const DropParams& drop,
                       hipStream_t stream);

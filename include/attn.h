@@ -22,7 +22,11 @@
  *     scores, natural log) and delta (D_i = sum_k dO_ik O_ik) are fp32 [B, H, N].
  *   - causal = 1 lets query i attend keys j <= i (square, top-left aligned);
  *     causal = 0 attends all N keys.
- *   - scale must be finite and > 0 (usually 1/sqrt(d)).
+ *   - scale is any finite value (usually 1/sqrt(d)).  A negative scale is
+ *     the same attention with the sign of every score flipped; scale = 0
+ *     gives uniform attention over the allowed keys (L = ln of their count,
+ *     dQ = dK = 0).  The kernels run the softmax with |scale| and apply the
+ *     sign to an operand they hold in registers (exact for bf16 and e4m3).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it and returns; it never synchronises.  The caller owns
  *     all buffers and keeps them alive until the stream has passed the work.
@@ -47,7 +51,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 6
+#define ATTN_ABI_VERSION 7
 
 typedef enum {
   ATTN_OK = 0,
@@ -231,8 +235,9 @@ attn_status_t attn_decode(const void* q, const void* k_cache, const void* v_cach
  * most [2^-4 sum_j p_j |v_j| + 2^-10 sum_{p_j < 2^-6} |v_j|] / sum_j p_j
  * (p_j = e^(S_j - max S) of its row) plus the bf16 rounding of O.
  *   q, k, v : [B, H, N, d] uint8 e4m3 codes, 16-byte aligned; NaN codes give NaN.
- *   descale_q, descale_k, descale_v : finite and > 0; scale * descale_q *
- *             descale_k must be a finite positive fp32 value.
+ *   descale_q, descale_k, descale_v : finite and > 0; scale is any finite
+ *             value, and |scale * descale_q * descale_k| must be a finite
+ *             fp32 value that is not 0 unless scale is 0.
  *   o   : output [B, H, N, d] bf16 (round to nearest even).
  *   lse : output [B, H, N] fp32.
  * Supported: d in {64, 128}, N <= 2^22 (ATTN_ERR_UNSUPPORTED otherwise);

@@ -77,9 +77,10 @@ def test_fwd_validation(lib):
     assert fwd(lib, H=-1) == INV
     assert fwd(lib, N=0) == INV
     assert fwd(lib, B=1 << 16, H=1 << 16, N=1) == INV  # B*H*N >= 2^31
-    assert fwd(lib, scale=0.0) == INV
-    assert fwd(lib, scale=-1.0) == INV
+    # any finite scale is accepted (a negative or zero one is valid attention;
+    # such calls would launch, so they are exercised by the GPU parity tests)
     assert fwd(lib, scale=float("nan")) == INV
+    assert fwd(lib, scale=float("-inf")) == INV
     assert fwd(lib, scale=float("inf")) == INV
     assert fwd(lib, causal=2) == INV
     assert fwd(lib, d=96) == UNS
@@ -102,7 +103,7 @@ def test_bwd_validation(lib):
         assert bwd(p) == INV, i
     assert bwd(ws_bytes=ws - 1) == INV
     assert bwd(N=0) == INV
-    assert bwd(scale=-0.5) == INV
+    assert bwd(scale=float("nan")) == INV
     assert bwd(causal=-1) == INV
     assert bwd(d=32) == UNS
     assert bwd(dtype=0) == UNS  # fp32 backward is not provided
@@ -124,7 +125,7 @@ def test_bwd_validation(lib):
     assert lib.attn_bwd_dq_fused(*([FAKE] * 8), 1, 1, (1 << 22) + 1, 64, 1, 0.1, 0, None) == UNS
     assert lib.attn_bwd_dq_fused(*([FAKE] * 8), 1, 1, 8, 96, 1, 0.1, 0, None) == UNS
     assert lib.attn_bwd_dq_fused(*([FAKE] * 8), 1, 1, 8, 64, 0, 0.1, 0, None) == UNS
-    assert lib.attn_bwd_dq_fused(*([FAKE] * 8), 1, 1, 8, 64, 1, 0.0, 0, None) == INV
+    assert lib.attn_bwd_dq_fused(*([FAKE] * 8), 1, 1, 8, 64, 1, float("nan"), 0, None) == INV
     assert lib.attn_bwd_dq_fused(*([FAKE] * 8), 1, 1, 8, 64, 1, 0.1, 2, None) == INV
 
 
@@ -143,7 +144,7 @@ def test_block_sparse_validation(lib):
     assert fwd_s(mh=0) == INV
     assert fwd_s(mh=3) == INV  # neither 1 nor B*H = 2
     assert fwd_s(causal=3) == INV
-    assert fwd_s(scale=0.0) == INV
+    assert fwd_s(scale=float("inf")) == INV
     assert fwd_s(N=65536 + 1) == UNS  # longest block-sparse sequence is 65536
     assert fwd_s(dtype=0) == UNS  # fp32 block-sparse is not provided
     assert fwd_s(d=80) == UNS
@@ -239,8 +240,12 @@ def test_fp8_validation(lib):
         p[i] = None
         assert f8(p) == INV, i
     for bad in (0.0, -1.0, float("inf"), float("nan")):
-        assert f8(dq=bad) == INV and f8(dk=bad) == INV and f8(dv=bad) == INV and f8(scale=bad) == INV
+        assert f8(dq=bad) == INV and f8(dk=bad) == INV and f8(dv=bad) == INV
+    for bad in (float("inf"), float("-inf"), float("nan")):
+        assert f8(scale=bad) == INV
     assert f8(dq=1e-30, dk=1e-30) == INV  # scale dq dk underflows fp32
+    assert f8(dq=1e-30, dk=1e-30, scale=-0.088) == INV  # |scale dq dk| underflows fp32
+    assert f8(dq=1e30, dk=1e30) == INV  # overflows
     assert f8(N=0) == INV
     assert f8(causal=2) == INV
     assert f8(d=96) == UNS
@@ -260,11 +265,31 @@ def test_binding_checks_block_mask_shape():
 
 
 def test_binding_refuses_cpu_tensors():
+    """Every tensor-taking entry point of the binding refuses CPU tensors before
+    any pointer reaches the library (no GPU is needed: the check comes first)."""
     import torch
 
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
-    with pytest.raises(ValueError):
-        binding.fwd(q, q, q)
+    f = torch.zeros(1, 1, 4, dtype=torch.float32)
+    m = torch.ones(1, 1, 1, dtype=torch.uint8)
+    u8 = torch.zeros(1, 1, 4, 64, dtype=torch.uint8)
+    calls = {
+        "fwd": lambda: binding.fwd(q, q, q),
+        "bwd": lambda: binding.bwd(q, q, q, q, f, q),
+        "bwd_preprocess": lambda: binding.bwd_preprocess(q, q),
+        "bwd_dkdv": lambda: binding.bwd_dkdv(q, q, q, f, q, f),
+        "bwd_dq": lambda: binding.bwd_dq(q, q, q, f, q, f),
+        "bwd_dq_fused": lambda: binding.bwd_dq_fused(q, q, q, q, f, q),
+        "fwd_block_sparse": lambda: binding.fwd_block_sparse(q, q, q, m),
+        "bwd_block_sparse": lambda: binding.bwd_block_sparse(q, q, q, q, f, q, m),
+        "fwd_dropout": lambda: binding.fwd_dropout(q, q, q, 0.1, 1),
+        "bwd_dropout": lambda: binding.bwd_dropout(q, q, q, q, f, q, 0.1, 1),
+        "decode": lambda: binding.decode(q, q, q),
+        "fwd_fp8": lambda: binding.fwd_fp8(u8, u8, u8, 1.0, 1.0, 1.0),
+    }
+    for name, call in calls.items():
+        with pytest.raises(ValueError):
+            call()
 
 
 def test_autograd_wrapper_refuses_cpu_tensors():
@@ -275,3 +300,4 @@ def test_autograd_wrapper_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         attention(q, q, q)
+

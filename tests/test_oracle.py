@@ -44,7 +44,7 @@ def test_worked_example_matches_printed_values():
     for key, spec in g["printed"].items():
         tol = 0.5 * 10 ** (-spec["decimals"]) + 1e-12
         assert abs(got[key] - spec["value"]) <= tol, (key, got[key], spec)
-    # block one's sum scaled to its own max is e^-1 + e^0 (page: "E the minus1 + E to the 0")
+    # block one's sum scaled to its own max is e^-1 + e^0 (video page, transcript 05:49, worked example)
     assert abs(bs1 - (math.exp(-1) + 1.0)) < 1e-15
     # the online result equals the textbook softmax denominator scaled to the final max
     assert m == 3.0 and abs(l - float(np.exp(np.array(g["scores"]) - 3.0).sum())) < 1e-15

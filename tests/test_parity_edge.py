@@ -1,0 +1,286 @@
+"""GPU edge cases of the bf16/fp32 path through the C ABI, against the fp64 oracle.
+
+* Any finite scale ("What is Flash Attention?", transcript 01:04: the scores
+  are Q K^T times a scale): a negative scale and scale = 0 (uniform attention
+  over the allowed keys), forward and backward, and the fp32, FP8 and decode
+  entry points at a negative scale.
+* The lazy rescale of the running max (slides, online-update formula; the
+  kernels raise the reference max only when a tile's max passes it by more
+  than 2^8): scores that climb by just under and just over 8 log2 units per
+  64-key tile, so the rescale branch runs every second tile or every tile and
+  unnormalised probabilities up to 2^8 are rounded and summed.
+* A sharp softmax (scale 2 on N(0, 1) inputs: nearly one-hot rows; slides,
+  safe-softmax formula).
+* A NaN in one query row stays in that row of O, L and dQ.
+* A rejected call (bad size, scale, causal flag, workspace or head dimension)
+  leaves real output buffers bit for bit unchanged.
+"""
+import ctypes
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import attention as orc
+from oracle import decode as orc_dec
+from oracle import fp8 as orc8
+from tests.checks import check_bf16, check_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def attn():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import exact_io_aware_23_amd as A
+
+    A.load_library()
+    return A
+
+
+def run_gpu(attn, inp, scale, causal, backward=True):
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    o, lse = attn.fwd(q, k, v, scale=scale, causal=causal)
+    out = {"o": o, "lse": lse}
+    if backward:
+        dq, dk, dv = attn.bwd(q, k, v, o, lse, inp["do"].cuda(), scale=scale, causal=causal)
+        out.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return {n: t.float().cpu() for n, t in out.items()}
+
+
+def compare_oracle(got, inp, scale, causal, tag, backward=True, rows=None, dq_rel_fro=None):
+    """Every element (or the listed query rows of O, L, dQ) of every head against the oracle.
+    dq_rel_fro, when given, replaces the relative-Frobenius gate for dQ (the
+    max-abs gate stays)."""
+    q, k, v = (inp[x].float().numpy() for x in ("q", "k", "v"))
+    do = inp["do"].float().numpy() if backward else None
+    B, H = q.shape[:2]
+    for b in range(B):
+        for h in range(H):
+            o_ref, l_ref, _ = orc.forward_head(q[b, h], k[b, h], v[b, h], scale, causal)
+            refs = {"o": o_ref, "lse": l_ref}
+            if backward:
+                dq_ref, dk_ref, dv_ref, _ = orc.backward_head(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
+                refs.update(dq=dq_ref, dk=dk_ref, dv=dv_ref)
+            for name, ref in refs.items():
+                g = got[name][b, h].numpy()
+                if rows is not None:
+                    if name not in ("o", "lse", "dq"):
+                        continue
+                    g, ref = g[rows], ref[rows]
+                if name == "dq" and dq_rel_fro is not None:
+                    check_bf16(f"{tag} {name}[{b},{h}]", g, ref, rel_fro=dq_rel_fro)
+                else:
+                    check_bf16(f"{tag} {name}[{b},{h}]", g, ref)
+
+
+# ---------------------------------------------------------------- any finite scale
+@pytest.mark.parametrize("scale", [-0.125, 0.0])
+@pytest.mark.parametrize("N,d,causal", [(300, 64, True), (333, 128, False), (1000, 128, True), (130, 64, False)])
+def test_scale_sign(attn, scale, N, d, causal):
+    inp = W.draw(1, 2, N, d, "bf16", seed=31 * N + d)
+    _say(f"scale={scale} N={N} d={d} causal={causal}")
+    got = run_gpu(attn, inp, scale, causal)
+    compare_oracle(got, inp, scale, causal, f"scale={scale} N={N}")
+    if scale == 0.0:
+        # uniform attention: dQ = dK = 0 exactly, L = ln(#allowed keys)
+        assert got["dq"].abs().max() == 0 and got["dk"].abs().max() == 0
+        n_allowed = np.arange(1, N + 1) if causal else np.full(N, N)
+        assert np.abs(got["lse"].numpy() - np.log(n_allowed)).max() < 1e-5
+
+
+def test_negative_scale_mirrors_negated_keys(attn):
+    """scale -s on (Q, K) is scale s on (Q, -K) (bf16 negation is exact).  The
+    scores are the same products on both sides, so O, L, dV and (with its sign
+    flipped) dK agree bit for bit.  dQ sums dS K on one side and dS (-K) on the
+    other; the matrix instruction's sum need not round symmetrically under
+    negation, so dQ is held to one bf16 ulp."""
+    inp = W.draw(1, 2, 257, 128, "bf16", seed=77)
+    neg = dict(inp, k=-inp["k"])
+    a = run_gpu(attn, inp, -0.09, True)
+    b = run_gpu(attn, neg, 0.09, True)
+    for n in ("o", "lse", "dv"):
+        assert torch.equal(a[n], b[n]), n
+    assert torch.equal(a["dk"], -b["dk"])
+    assert ((a["dq"] - b["dq"]).abs() <= 2.0 ** -7 * a["dq"].abs() + 1e-30).all()
+
+
+@pytest.mark.parametrize("scale", [-0.125, 0.0])
+def test_scale_sign_fp32_forward(attn, scale):
+    inp = W.draw(1, 2, 200, 64, "f32", seed=5, backward=False)
+    got = run_gpu(attn, inp, scale, True, backward=False)
+    q, k, v = (inp[x].numpy() for x in ("q", "k", "v"))
+    for h in range(2):
+        o_ref, l_ref, _ = orc.forward_head(q[0, h], k[0, h], v[0, h], scale, True)
+        check_f32(f"fp32 scale={scale} O[{h}]", got["o"][0, h], o_ref)
+        check_f32(f"fp32 scale={scale} L[{h}]", got["lse"][0, h], l_ref)
+
+
+def test_negative_scale_fp8(attn):
+    """attn_fwd_fp8 at a negative scale equals the positive scale on negated
+    K codes (e4m3 negation flips the sign bit), bit for bit."""
+    inp = W.draw_fp8(1, 2, 300, 128, seed=9)
+    q8, k8, v8 = (inp[x].cuda() for x in ("q8", "k8", "v8"))
+    k8n = (k8.view(torch.uint8) ^ 0x80).view(k8.dtype)
+    o1, l1 = attn.fwd_fp8(q8, k8, v8, inp["dq"], inp["dk"], inp["dv"], scale=-0.088, causal=True)
+    o2, l2 = attn.fwd_fp8(q8, k8n, v8, inp["dq"], inp["dk"], inp["dv"], scale=0.088, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # and against the oracle: L is the logsumexp of the dequantized scores
+    qh, kh, vh = (inp[x][0, 0].numpy() for x in ("q8", "k8", "v8"))
+    o_ref, l_ref = orc8.forward_head_fp8(qh, kh, vh, inp["dq"], inp["dk"], inp["dv"], -0.088, True)[:2]
+    assert np.abs(l1[0, 0].cpu().numpy() - l_ref).max() < 2e-2
+    assert np.isfinite(o1.float().cpu().numpy()).all()
+
+
+@pytest.mark.parametrize("scale", [-0.1, 0.0])
+def test_scale_sign_decode(attn, scale):
+    B, H, Nq, Nk, d = 1, 2, 4, 1500, 128
+    cache = W.draw(B, H, Nk, d, "bf16", seed=61, backward=False)
+    q = W.draw(B, H, Nq, d, "bf16", seed=62, backward=False)["q"]
+    o, lse = attn.decode(q.cuda(), cache["k"].cuda(), cache["v"].cuda(), scale=scale, causal=True)
+    torch.cuda.synchronize()
+    for h in range(H):
+        o_ref, l_ref = orc_dec.decode_head(q[0, h].double().numpy(), cache["k"][0, h].double().numpy(),
+                                           cache["v"][0, h].double().numpy(), scale, True)
+        check_bf16(f"decode scale={scale} O[{h}]", o[0, h], o_ref)
+        check_bf16(f"decode scale={scale} L[{h}]", lse[0, h], l_ref)
+
+
+# ---------------------------------------------------------------- the lazy rescale
+def _ramp_inputs(N, d, scale, climb, causal, seed):
+    """Scores that rise by `climb` log2 units per 64 keys: q_i = t e_0 and
+    k_j = (j / 64) e_0 plus small N(0, 0.1^2) noise in the other columns, with
+    t = climb / (scale log2 e), both rounded to bf16 like every input.
+    (The large factor sits in Q: dQ uses delta~ = rowsum(dO * O) over the
+    stored bf16 O, whose rounding error is multiplied by sum_j P_ij K_j, so
+    keys of magnitude ~N would test that reading instead of the rescale.)"""
+    g = torch.Generator().manual_seed(seed)
+    t = climb / (scale * math.log2(math.e))
+    q = 0.1 * torch.randn(1, 2, N, d, generator=g)
+    k = 0.1 * torch.randn(1, 2, N, d, generator=g)
+    v = torch.randn(1, 2, N, d, generator=g)
+    do = torch.randn(1, 2, N, d, generator=g)
+    q[..., 0] = t
+    k[..., 0] = torch.arange(N, dtype=torch.float32) / 64.0
+    return {n: x.to(torch.bfloat16) for n, x in (("q", q), ("k", k), ("v", v), ("do", do))}
+
+
+@pytest.mark.parametrize("climb", [7.9, 8.1])
+@pytest.mark.parametrize("d,causal", [(64, True), (64, False), (128, True), (128, False)])
+def test_lazy_rescale_climbing_scores(attn, climb, d, causal):
+    N = 333  # five 64-key tiles and a ragged tail
+    scale = 1 / math.sqrt(d)
+    inp = _ramp_inputs(N, d, scale, climb, causal, seed=int(10 * climb) + d + causal)
+    _say(f"ramp climb={climb}/tile d={d} causal={causal}")
+    got = run_gpu(attn, inp, scale, causal)
+    # dQ is formed with delta~ = rowsum(dO * O) over the stored bf16 O (as the
+    # backward takes it); that delta's rounding error (~2^-9 |dO| |O|) times
+    # sum_j P_ij K_j is a few per cent of these small, cancelling dQ rows, so
+    # dQ keeps the max-abs gate but gets 5e-2 on the relative-Frobenius one
+    compare_oracle(got, inp, scale, causal, f"ramp {climb} d={d} c={causal}", dq_rel_fro=5e-2)
+
+
+def test_sharp_softmax(attn):
+    inp = W.draw(1, 2, 640, 64, "bf16", seed=91)
+    _say("sharp softmax, scale 2")
+    for causal in (False, True):
+        got = run_gpu(attn, inp, 2.0, causal)
+        compare_oracle(got, inp, 2.0, causal, f"sharp c={causal}")
+
+
+# ---------------------------------------------------------------- non-finite input
+@pytest.mark.parametrize("d,causal", [(64, True), (128, False)])
+def test_nan_stays_in_its_row(attn, d, causal):
+    N, row = 300, 137
+    inp = W.draw(1, 1, N, d, "bf16", seed=17 + d)
+    inp["q"][0, 0, row, 5] = float("nan")
+    got = run_gpu(attn, inp, 1 / math.sqrt(d), causal)
+    for name in ("o", "lse", "dq"):
+        t = got[name][0, 0]
+        assert torch.isnan(t[row]).all(), f"{name}: row {row} should be NaN"
+        others = torch.cat([t[:row], t[row + 1:]])
+        assert torch.isfinite(others).all(), f"{name}: NaN leaked out of row {row}"
+    rows = [i for i in range(N) if i != row]
+    compare_oracle(got, inp, 1 / math.sqrt(d), causal, f"NaN row d={d}", rows=rows)
+
+
+# ---------------------------------------------------------------- rejected calls
+def test_rejected_calls_leave_outputs_untouched(attn):
+    lib = attn.load_library()
+    B, H, N, d = 1, 2, 256, 64
+    inp = W.draw(B, H, N, d, "bf16", seed=3)
+    q, k, v, do = (inp[x].cuda() for x in ("q", "k", "v", "do"))
+    sentinel = torch.tensor(-12345.0, dtype=torch.bfloat16)
+    o, dq, dk, dv = (torch.full_like(q, sentinel) for _ in range(4))
+    lse = torch.full((B, H, N), -777.0, dtype=torch.float32, device=q.device)
+    ws_bytes = attn.bwd_workspace_bytes(B, H, N, d)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)
+    before = [t.clone() for t in (o, lse, dq, dk, dv)]
+    st = torch.cuda.current_stream().cuda_stream
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    nan = float("nan")
+
+    def fwd(N_=N, d_=d, dtype=1, scale=0.125, causal=0, qp=None):
+        return lib.attn_fwd(qp if qp is not None else P(q), P(k), P(v), P(o), P(lse), B, H, N_, d_, dtype, scale,
+                            causal, st)
+
+    def bwd(N_=N, d_=d, dtype=1, scale=0.125, causal=0, wsb=ws_bytes):
+        return lib.attn_bwd(P(q), P(k), P(v), P(o), P(lse), P(do), P(dq), P(dk), P(dv), P(ws), wsb, B, H, N_, d_,
+                            dtype, scale, causal, st)
+
+    INV, UNS = 1, 2
+    assert fwd(qp=ctypes.c_void_p(0)) == INV
+    assert fwd(N_=0) == INV
+    assert fwd(scale=nan) == INV
+    assert fwd(scale=float("inf")) == INV
+    assert fwd(causal=2) == INV
+    assert fwd(d_=96) == UNS
+    assert fwd(dtype=7) == UNS
+    assert bwd(wsb=ws_bytes - 1) == INV
+    assert bwd(scale=nan) == INV
+    assert bwd(causal=-1) == INV
+    assert bwd(d_=80) == UNS
+    assert bwd(dtype=0) == UNS
+    assert bwd(N_=(1 << 22) + 1) == UNS
+    torch.cuda.synchronize()
+    for a, b_ in zip(before, (o, lse, dq, dk, dv)):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b_.view(torch.uint8) if b_.dtype == torch.bfloat16 else b_.view(torch.int32))
+    # and a valid call afterwards does write them
+    assert fwd() == 0
+    torch.cuda.synchronize()
+    assert not torch.equal(o, before[0])
+
+
+def test_binding_refuses_one_cpu_tensor(attn):
+    """Each entry point checks every tensor it passes on, not only the first:
+    one CPU tensor among GPU ones is refused before the library is called."""
+    B, H, N, d = 1, 1, 8, 64
+    g = {n: torch.zeros(B, H, N, d, dtype=torch.bfloat16, device="cuda") for n in ("q", "k", "v", "o", "do")}
+    f = torch.zeros(B, H, N, dtype=torch.float32, device="cuda")
+    calls = {
+        "bwd_dkdv": lambda t: attn.bwd_dkdv(t["q"], t["k"], t["v"], f, t["do"], f),
+        "bwd_dq": lambda t: attn.bwd_dq(t["q"], t["k"], t["v"], f, t["do"], f),
+        "bwd_dq_fused": lambda t: attn.bwd_dq_fused(t["q"], t["k"], t["v"], t["o"], f, t["do"]),
+        "bwd_preprocess": lambda t: attn.bwd_preprocess(t["o"], t["do"]),
+        "bwd": lambda t: attn.bwd(t["q"], t["k"], t["v"], t["o"], f, t["do"]),
+    }
+    used = {"bwd_dkdv": "qkv d", "bwd_dq": "qkv d", "bwd_dq_fused": "qkvod", "bwd_preprocess": "od", "bwd": "qkvod"}
+    names = {"q": "q", "k": "k", "v": "v", "o": "o", "d": "do"}
+    for fn, call in calls.items():
+        for c in used[fn].replace(" ", ""):
+            t = dict(g)
+            t[names[c]] = g[names[c]].cpu()
+            with pytest.raises(ValueError):
+                call(t)

@@ -155,6 +155,39 @@ def test_fp8_full_size_sampled_rows(attn, B, H, N, d, causal, count):
               np.array(cols[3]), np.stack(cols[4]), np.stack(cols[5]), np.array(cols[6]))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_score_error_within_s_rel(attn, d):
+    """Pins S_REL through the entry point itself.  With N = 1 each row has one
+    key, so L is exactly its score s = scale dq dk sum_k q_k k_k (p = 1, l = 1)
+    and O is the value row.  Over 524288 rows of random e4m3 codes (four seeds)
+    the matrix instruction's dot products must stay within
+    |L - s| <= S_REL |scale dq dk| sum_k |q_k k_k| + 2^-18 |s|
+    of the fp64 dot products of the decoded codes; the largest error seen is
+    printed as a multiple of S_REL."""
+    B, H, N = 256, 512, 1
+    scale = 1 / math.sqrt(d)
+    worst, worst_rel = 0.0, 0.0
+    for seed in range(4):
+        inp = W.draw_fp8(B, H, N, d, seed=7800 + 10 * d + seed)
+        o, lse = run(attn, inp, scale, False)
+        q = orc8.e4m3_decode(inp["q8"].numpy()).reshape(-1, d)
+        k = orc8.e4m3_decode(inp["k8"].numpy()).reshape(-1, d)
+        v = orc8.e4m3_decode(inp["v8"].numpy()).reshape(-1, d) * inp["dv"]
+        f = scale * inp["dq"] * inp["dk"]
+        s = f * (q * k).sum(axis=1)
+        mag = abs(f) * np.abs(q * k).sum(axis=1)
+        err = np.abs(lse.reshape(-1).astype(np.float64) - s)
+        bound = S_REL * mag + 2.0 ** -18 * np.abs(s)
+        assert (err <= bound).all(), f"seed {seed}: max err/bound {(err / bound).max():.3f}"
+        worst = max(worst, float((err / bound).max()))
+        worst_rel = max(worst_rel, float((np.maximum(err - 2.0 ** -18 * np.abs(s), 0) / mag).max()))
+        # O is the (bf16-rounded) value row
+        ov = o.reshape(-1, d).astype(np.float64)
+        assert (np.abs(ov - v) <= 2.0 ** -8 * np.abs(v) + 1e-30).all()
+    _say(f"d={d}: 4 x {B * H} rows, max |L - s| / bound = {worst:.3f}; score error up to "
+         f"{worst_rel / S_REL:.3f} S_REL = 2^{math.log2(max(worst_rel, 1e-30)):.2f} of scale dq dk sum|q k|")
+
+
 def test_fp8_is_deterministic(attn):
     inp = W.draw_fp8(1, 4, 1000, 128, seed=7600)
     dev = [inp[x].cuda() for x in ("q8", "k8", "v8")]
