@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     bwd_dropout,
     bwd_dq,
     bwd_dq_fused,
+    bwd_noalloc,
+    bwd_noalloc_max_rows,
     bwd_preprocess,
     bwd_workspace_bytes,
     decode,

@@ -11,7 +11,7 @@ import torch
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libattn.so")
 
-ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP, ATTN_ERR_SCRATCH = 0, 1, 2, 3, 4
 ATTN_F32, ATTN_BF16 = 0, 1
 
 _lib = None
@@ -27,6 +27,8 @@ _SIGNATURES = {
     "attn_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_workspace_bytes": (_S, [_I, _I, _I, _I]),
     "attn_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "attn_bwd_noalloc_max_rows": (_S, []),
     "attn_bwd_preprocess": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P]),
     "attn_bwd_dkdv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "attn_bwd_dq": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
@@ -175,6 +177,28 @@ def bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, w
     _call("attn_bwd", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, N, d,
           _dtype_code(q), _default_scale(d, scale), int(bool(causal)), _stream(q.device))
+    return dq, dk, dv
+
+
+def bwd_noalloc_max_rows() -> int:
+    return int(load_library().attn_bwd_noalloc_max_rows())
+
+
+def bwd_noalloc(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False, dq=None, dk=None, dv=None):
+    """attn_bwd_noalloc (no workspace: the library's static scratch array); returns (dQ, dK, dV).
+    dq, dk, dv are allocated here when not given; the library call itself allocates nothing."""
+    B, H, N, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    _check("lse", lse, (B, H, N), torch.float32)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check(name, t, (B, H, N, d), q.dtype)
+    _call("attn_bwd_noalloc", q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+          dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, _dtype_code(q), _default_scale(d, scale),
+          int(bool(causal)), _stream(q.device))
     return dq, dk, dv
 
 

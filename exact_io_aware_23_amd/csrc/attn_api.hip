@@ -3,6 +3,7 @@
 // work is launched and no output is touched.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/attn.h"
 #include "attn_launch.h"
@@ -165,6 +166,58 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                  attn::DropParams{}, stream);
 }
 
+}  // extern "C"
+
+namespace {
+// Scratch of attn_bwd_noalloc: the exact delta of the dq stage, one fp32 per
+// query row, in a file-scope device array instead of a caller workspace.  Each
+// GPU holds its own copy until the process ends.  In host code `scratch`
+// names a host-side stand-in; kernels get the device address that
+// hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)16 << 20;  // 4M rows
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of this device's scratch array (the current device)
+attn_status_t scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ATTN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t attn_bwd_noalloc_max_rows(void) { return kScratchBytes / sizeof(float); }
+
+attn_status_t attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                               const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                               attn_dtype_t dtype, float scale, int causal, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_INVALID;
+  if (!sizes_ok(B, H, N) || !scale_ok(scale) || (causal != 0 && causal != 1)) return ATTN_ERR_INVALID;
+  if (N > kMaxN) return ATTN_ERR_UNSUPPORTED;
+  const attn_status_t s = check_bf16_d(d, dtype);
+  if (s != ATTN_OK) return s;
+  if (attn_bwd_workspace_bytes(B, H, N, d) > kScratchBytes) return ATTN_ERR_SCRATCH;
+  void* ws = nullptr;
+  const attn_status_t sa = scratch_address(&ws);
+  if (sa != ATTN_OK) return sa;
+  // every row of the delta array is written by the dq stage before the dkdv
+  // stage reads it, so the previous call's contents need no clearing
+  return bwd_all(q, k, v, o, lse, dout, dq, dk, dv, ws, B, H, N, d, scale, causal, attn::BlockMask{},
+                 attn::DropParams{}, stream);
+}
+
 attn_status_t attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
                                     const uint8_t* block_mask, int mask_heads, int B, int H, int N, int d,
                                     attn_dtype_t dtype, float scale, int causal, void* stream) {
@@ -268,6 +321,7 @@ const char* attn_status_string(attn_status_t s) {
     case ATTN_ERR_INVALID: return "invalid argument";
     case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension, dtype or sequence length";
     case ATTN_ERR_HIP: return "HIP launch error";
+    case ATTN_ERR_SCRATCH: return "problem larger than the static scratch buffer of the allocation-free entry point";
   }
   return "unknown status";
 }

@@ -30,8 +30,9 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it and returns; it never synchronises.  The caller owns
  *     all buffers and keeps them alive until the stream has passed the work.
- *   - The library allocates no device memory and keeps no global state; calls
- *     on different streams may run concurrently.
+ *   - The library allocates no device memory and keeps no global state, except
+ *     the static scratch array of attn_bwd_noalloc (see there); calls of the
+ *     other entry points on different streams may run concurrently.
  *   - Validation happens before anything is enqueued.  On any error nothing is
  *     launched and no output is written.  ATTN_OK means "enqueued"; a device
  *     fault shows up at the caller's next synchronisation.
@@ -51,13 +52,14 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 7
+#define ATTN_ABI_VERSION 8
 
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID = 1,     /* null pointer, non-positive size, bad scale/causal, workspace too small */
   ATTN_ERR_UNSUPPORTED = 2, /* d, dtype or (block-sparse) N outside the supported set */
-  ATTN_ERR_HIP = 3          /* the HIP runtime refused a launch */
+  ATTN_ERR_HIP = 3,         /* the HIP runtime refused a launch */
+  ATTN_ERR_SCRATCH = 4      /* attn_bwd_noalloc: B*H*N above attn_bwd_noalloc_max_rows() */
 } attn_status_t;
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype_t;
@@ -93,6 +95,29 @@ attn_status_t attn_bwd(const void* q, const void* k, const void* v, const void* 
                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
                        void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                        attn_dtype_t dtype, float scale, int causal, void* stream);
+
+/* Backward pass that allocates nothing, for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, kernels
+ * and results (bit for bit) as attn_bwd, without the workspace: the exact
+ * delta the dq stage hands to the dkdv stage goes to a static device array of
+ * 16 MiB that the library holds on each GPU until the process ends.
+ *   - B*H*N must be at most attn_bwd_noalloc_max_rows() (4194304), else
+ *     ATTN_ERR_SCRATCH and nothing is launched.
+ *   - `stream` must belong to the current device; the first call on a device
+ *     looks up that device's array (hipGetSymbolAddress) and keeps it.
+ *   - Calls on one GPU share its array: two calls whose work overlaps in time
+ *     on that GPU (different streams, no ordering between them) race and give
+ *     wrong results.  Calls ordered on one stream are fine; the array keeps
+ *     the last call's contents, and every entry is rewritten before it is read.
+ *   - It calls no hipMalloc, hipFree or other allocating routine. */
+attn_status_t attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               int B, int H, int N, int d, attn_dtype_t dtype, float scale,
+                               int causal, void* stream);
+
+/* Largest B*H*N attn_bwd_noalloc accepts. */
+size_t attn_bwd_noalloc_max_rows(void);
 
 /* Backward stage 1: delta~_i = sum_k dO_ik * O_ik in fp32.  Mathematically
  * equal to sum_j P_ij dP_ij (the row term of the softmax Jacobian); with O

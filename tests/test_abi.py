@@ -35,7 +35,7 @@ def test_header_declares_the_expected_entry_points():
         "attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_bwd_preprocess", "attn_bwd_dkdv",
         "attn_bwd_dq", "attn_bwd_dq_fused", "attn_status_string", "attn_abi_version", "attn_fwd_block_sparse",
         "attn_bwd_block_sparse", "attn_fwd_dropout", "attn_bwd_dropout", "attn_decode_workspace_bytes",
-        "attn_decode", "attn_fwd_fp8"])
+        "attn_decode", "attn_fwd_fp8", "attn_bwd_noalloc", "attn_bwd_noalloc_max_rows"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -53,7 +53,7 @@ def test_abi_version_matches_header(lib):
 
 
 def test_status_strings(lib):
-    for s in range(4):
+    for s in range(5):
         assert lib.attn_status_string(s)
     assert lib.attn_status_string(99) == b"unknown status"
 
@@ -301,3 +301,26 @@ def test_autograd_wrapper_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         attention(q, q, q)
 
+
+def test_noalloc_validation(lib):
+    """attn_bwd_noalloc validates like attn_bwd and rejects problems larger than
+    its static scratch array with ATTN_ERR_SCRATCH, before any launch."""
+    INV, UNS, SCR = binding.ATTN_ERR_INVALID, binding.ATTN_ERR_UNSUPPORTED, binding.ATTN_ERR_SCRATCH
+    rows = lib.attn_bwd_noalloc_max_rows()
+    assert rows == (16 << 20) // 4
+
+    def call(ptrs=None, B=1, H=2, N=100, d=64, dtype=1, scale=0.125, causal=1):
+        p = ptrs or [FAKE] * 9
+        return lib.attn_bwd_noalloc(*p, B, H, N, d, dtype, scale, causal, None)
+
+    for i in range(9):
+        p = [FAKE] * 9
+        p[i] = None
+        assert call(p) == INV, i
+    assert call(N=0) == INV
+    assert call(scale=float("nan")) == INV
+    assert call(causal=2) == INV
+    assert call(d=96) == UNS
+    assert call(dtype=0) == UNS
+    assert call(B=2, H=2, N=(1 << 20) + 1) == SCR  # one row past the scratch array
+    assert call(B=1, H=3, N=1 << 21) == SCR
