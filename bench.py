@@ -71,6 +71,8 @@ def parse():
                     help="fwd: time the forward kernel alone (for profiling); copy: a plain 1 GiB device copy "
                          "(calibrates the HBM byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
+    ap.add_argument("--clock-seconds", type=float, default=1.5,
+                    help="after the timed steps, repeat the step this long while sampling the GPU clock (0: skip)")
     ap.add_argument("--dropout", type=float, default=None, help="time the dropout entry points at this rate")
     ap.add_argument("--fp8", action="store_true", help="time attn_fwd_fp8 (e4m3 inputs) on the workload's shape")
     ap.add_argument("--decode", type=int, default=None, help="time attn_decode with this many queries per head")
@@ -225,15 +227,37 @@ class ClockSampler:
             self._thread.join()
         return False
 
-    def mean(self):
-        return sum(self.samples) / len(self.samples) if self.samples else None
+    def settled(self):
+        """The samples of the second half of the window: the metrics table the
+        samples come from refreshes only every few hundred ms, so the first
+        samples of a window can still show the idle clock."""
+        return self.samples[len(self.samples) // 2:]
 
-    def report(self):
-        m = self.mean()
-        return {"gpu_clock_mhz_avg": round(m, 1) if m is not None else None, "gpu_clock_samples": len(self.samples),
-                "gpu_clock_source": "amdsmi gpu metrics (per-XCD current gfx clock), sampled every "
-                                    f"{self.period * 1e3:.0f} ms during the timed steps"
+    def mean(self):
+        s = self.settled()
+        return sum(s) / len(s) if s else None
+
+    def report(self, window_s: float):
+        m, s = self.mean(), self.settled()
+        return {"gpu_clock_mhz_avg": round(m, 1) if m is not None else None,
+                "gpu_clock_mhz_min_max": [round(min(s), 1), round(max(s), 1)] if s else None,
+                "gpu_clock_samples": len(s),
+                "gpu_clock_source": "amdsmi gpu metrics, mean over XCDs of the current gfx clock, sampled every "
+                                    f"{self.period * 1e3:.0f} ms while the same step repeats for {window_s:.1f} s "
+                                    "after the timed steps (second half of the window)"
                                     + (f"; {self.error}" if self.error else "")}
+
+
+def measure_clock(step, seconds: float):
+    """Repeat step() for `seconds` (outside any timed region) while sampling the clock."""
+    clock = ClockSampler(period=0.02)
+    torch.cuda.synchronize()
+    with clock:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            step()
+            torch.cuda.synchronize()
+    return clock
 
 
 COPY_BYTES = 1 << 30
@@ -673,14 +697,13 @@ def main():
     torch.cuda.synchronize()
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    clock = ClockSampler()
     torch.cuda.synchronize()
-    with clock:
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            step(events[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    clock = measure_clock(step, args.clock_seconds) if args.clock_seconds > 0 else None
 
     samples = {n: [ev[j].elapsed_time(ev[j + 1]) for ev in events] for j, n in enumerate(names)}
     per_kernel = {n: sum(t) / args.steps for n, t in samples.items()}  # ms per launch
@@ -736,9 +759,9 @@ def main():
         "kernel_ms_median": {n: round(sorted(t)[len(t) // 2], 4) for n, t in samples.items()},
         "kernel_ms_min": {n: round(min(t), 4) for n, t in samples.items()},
         "roofline": roof,
-        "host": {**host_facts(), **clock.report()},
+        "host": {**host_facts(), **(clock.report(args.clock_seconds) if clock else {})},
     }
-    if clock.mean() is not None:
+    if clock is not None and clock.mean() is not None:
         # the MFMA peak at the clock the kernels actually ran at, for context
         out["mfma_peak_at_measured_clock_tflops"] = round(MFMA_BF16_PEAK_TFLOPS * clock.mean() / 2400.0, 1)
     if not args.no_cpu_baseline:

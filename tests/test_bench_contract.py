@@ -38,3 +38,8 @@ def test_bench_json_line():
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert 0 < roof["frac"] < 1 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     assert "cpu_baseline" not in out
+    host = out["host"]
+    for key in ("cpu_model", "cpu_count", "affinity_cpus", "gpu_clock_mhz_avg", "gpu_clock_samples",
+                "gpu_clock_source"):
+        assert key in host, key
+    assert host["cpu_count"] >= host["affinity_cpus"] >= 1
