@@ -71,12 +71,15 @@ constexpr float kTau = 8.0f;
 // with the one-tile-at-a-time kernel: up to eight 64-key tiles per workgroup.
 constexpr int kShortSeqMaxN = 512;
 
-template <int D, bool CAUSAL, bool SPARSE, bool DROP, bool PIPE = true>
-__global__ void __launch_bounds__(256, PIPE ? 2 : 4)
-fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                bf16* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, int total, float c,
-                const uint8_t* __restrict__ Mask, int mask_hs, int nb, uint32_t drop_t, uint32_t seed_lo,
-                uint32_t seed_hi, float inv_keep, uint32_t smode) {
+// One work item (query tile qt of head bh, work = bh * n_qtiles + index) of
+// the forward, by one workgroup of 256 threads.
+template <int D, bool CAUSAL, bool SPARSE, bool DROP, bool PIPE>
+__device__ __forceinline__ void fwd_bf16_item(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                                              const bf16* __restrict__ V, bf16* __restrict__ O,
+                                              float* __restrict__ L, int N, int n_qtiles, float c,
+                                              const uint8_t* __restrict__ Mask, int mask_hs, int nb,
+                                              uint32_t drop_t, uint32_t seed_lo, uint32_t seed_hi, float inv_keep,
+                                              uint32_t smode, int work) {
   using C = FwdCfg<D>;
   static_assert(!(SPARSE && DROP), "block-sparse and dropout are separate entry points");
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * C::STAGE];
@@ -84,7 +87,6 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   __shared__ uint16_t tlist[SPARSE ? kMaxSparseN / C::BC : 1];
   __shared__ int wcnt[SPARSE ? 4 : 1];
 
-  const int work = xcd_remap(blockIdx.x, total);
   const int bh = work / n_qtiles;
   const int qt = CAUSAL ? (n_qtiles - 1 - work % n_qtiles) : (work % n_qtiles);
   const size_t head = (size_t)bh * N * D;
@@ -417,6 +419,40 @@ fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   }
 }
 
+// One work item per workgroup, in the XCD-aware order of xcd_remap.
+template <int D, bool CAUSAL, bool SPARSE, bool DROP, bool PIPE = true>
+__global__ void __launch_bounds__(256, PIPE ? 2 : 4)
+fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                bf16* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, int total, float c,
+                const uint8_t* __restrict__ Mask, int mask_hs, int nb, uint32_t drop_t, uint32_t seed_lo,
+                uint32_t seed_hi, float inv_keep, uint32_t smode) {
+  fwd_bf16_item<D, CAUSAL, SPARSE, DROP, PIPE>(Q, K, V, O, L, N, n_qtiles, c, Mask, mask_hs, nb, drop_t, seed_lo,
+                                               seed_hi, inv_keep, smode, xcd_remap(blockIdx.x, total));
+}
+
+// Causal forward with one pair of query tiles per workgroup: tile p and tile
+// n - 1 - p of the same head, one after the other, so every workgroup does
+// the same work (n + 1 tiles' worth) and the hardware's turn-based dispatch
+// over the XCDs never waits for a long tile.  Workgroup b runs on XCD b % 8
+// and takes pair b / 8 of that XCD's heads (the xcd_remap order), the shorter
+// tile first (measured within 0.5% of the other order).
+template <int D>
+__global__ void __launch_bounds__(256, 2)
+fwd_bf16_pair_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                     bf16* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, int total, float c,
+                     uint32_t smode) {
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int per_xcd = total >> 3, half = n_qtiles >> 1;
+  const int base = x * per_xcd + (j / half) * n_qtiles, p = j % half;
+  // item index i within a head is query tile n - 1 - i (longest first)
+  const int first = base + n_qtiles - 1 - p, second = base + p;
+  fwd_bf16_item<D, true, false, false, true>(Q, K, V, O, L, N, n_qtiles, c, nullptr, 0, 0, 0u, 0u, 0u, 1.f, smode,
+                                             first);
+  __syncthreads();  // every wave is done with the first tile's LDS before the second copies its own
+  fwd_bf16_item<D, true, false, false, true>(Q, K, V, O, L, N, n_qtiles, c, nullptr, 0, 0, 0u, 0u, 0u, 1.f, smode,
+                                             second);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 forward: the same online-softmax algorithm on plain fp32 VALU
 // arithmetic.  Four threads share a query row, each holding a quarter of its
@@ -492,6 +528,12 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
   }
 }
 
+// Longest causal sequence, in 128-row query tiles, that runs as pairs of tiles
+// per workgroup (measured: 2.6% faster at 64 tiles, 10% at 32; 1% slower at
+// 256, where each workgroup is long anyway and a second head's keys and
+// values compete for the XCD's L2).
+constexpr int kPairMaxQtiles = 64;
+
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                              int N, float scale, const BlockMask& m, const DropParams& dr, hipStream_t stream) {
@@ -517,6 +559,9 @@ hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* 
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, false, /*PIPE=*/!kShortFwd>), dim3(total), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
                        sc.c, (const uint8_t*)nullptr, 0, 0, 0u, 0u, 0u, 1.f, sc.mode);
+  else if (CAUSAL && !short_seq && BH % 8 == 0 && n_qtiles % 2 == 0 && n_qtiles <= kPairMaxQtiles)
+    hipLaunchKernelGGL((fwd_bf16_pair_kernel<D>), dim3(total / 2), dim3(256), 0, stream, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total, sc.c, sc.mode);
   else
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, false, false>), dim3(total), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, N, n_qtiles, total,
