@@ -210,6 +210,18 @@ __device__ __forceinline__ int xcd_remap(int wid, int total) {
   return (wid & 7) * (total >> 3) + (wid >> 3);
 }
 
+// Work item `item` (0 or 1) of workgroup b when each workgroup runs two
+// tiles of one head: tile p and tile n - 1 - p (n tiles per head, item index
+// i within a head, longest first).  Workgroup b runs on XCD b % 8 and takes
+// pair b / 8 of that XCD's work items (whole heads, as in xcd_remap); the
+// shorter tile comes first.  Needs (B H) % 8 == 0 and n even.
+__device__ __forceinline__ int pair_work(int b, int total, int n, int item) {
+  const int x = b & 7, j = b >> 3;
+  const int half = n >> 1;
+  const int base = x * (total >> 3) + (j / half) * n, p = j % half;
+  return item == 0 ? base + n - 1 - p : base + p;
+}
+
 // ---- dropout decisions: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011)
 // One call maps a 128-bit counter and a 64-bit key to 128 random bits: ten
 // rounds of two 32 x 32 -> 64-bit products, with the key advanced by two Weyl

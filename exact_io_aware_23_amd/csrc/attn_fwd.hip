@@ -441,11 +441,7 @@ __global__ void __launch_bounds__(256, 2)
 fwd_bf16_pair_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                      bf16* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, int total, float c,
                      uint32_t smode) {
-  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
-  const int per_xcd = total >> 3, half = n_qtiles >> 1;
-  const int base = x * per_xcd + (j / half) * n_qtiles, p = j % half;
-  // item index i within a head is query tile n - 1 - i (longest first)
-  const int first = base + n_qtiles - 1 - p, second = base + p;
+  const int first = pair_work(blockIdx.x, total, n_qtiles, 0), second = pair_work(blockIdx.x, total, n_qtiles, 1);
   fwd_bf16_item<D, true, false, false, true>(Q, K, V, O, L, N, n_qtiles, c, nullptr, 0, 0, 0u, 0u, 0u, 1.f, smode,
                                              first);
   __syncthreads();  // every wave is done with the first tile's LDS before the second copies its own

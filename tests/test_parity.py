@@ -99,7 +99,7 @@ SMALL = [
     # the last length the one-tile-at-a-time d=64 forward takes, and the first past it
     (1, 2, 512, 64, True), (1, 2, 513, 64, False),
     # causal with B*H a multiple of 8 and an even number of 128-row tiles: the
-    # forward runs two query tiles per workgroup (ragged last tile)
+    # forward and the dq kernel run two query tiles per workgroup (ragged last tile)
     (1, 8, 1000, 128, True), (2, 4, 900, 64, True),
 ]
 
