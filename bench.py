@@ -237,9 +237,17 @@ class ClockSampler:
         s = self.settled()
         return sum(s) / len(s) if s else None
 
+    def median(self):
+        """Median of the settled samples: one stray idle reading (the metrics
+        table can report one between steps) moves it far less than the mean."""
+        s = sorted(self.settled())
+        return s[len(s) // 2] if s else None
+
     def report(self, window_s: float):
         m, s = self.mean(), self.settled()
+        md = self.median()
         return {"gpu_clock_mhz_avg": round(m, 1) if m is not None else None,
+                "gpu_clock_mhz_median": round(md, 1) if md is not None else None,
                 "gpu_clock_mhz_min_max": [round(min(s), 1), round(max(s), 1)] if s else None,
                 "gpu_clock_samples": len(s),
                 "gpu_clock_source": "amdsmi gpu metrics, mean over XCDs of the current gfx clock, sampled every "
@@ -763,7 +771,7 @@ def main():
     }
     if clock is not None and clock.mean() is not None:
         # the MFMA peak at the clock the kernels actually ran at, for context
-        out["mfma_peak_at_measured_clock_tflops"] = round(MFMA_BF16_PEAK_TFLOPS * clock.mean() / 2400.0, 1)
+        out["mfma_peak_at_measured_clock_tflops"] = round(MFMA_BF16_PEAK_TFLOPS * clock.median() / 2400.0, 1)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, fwd_only)
     print(json.dumps(out), flush=True)

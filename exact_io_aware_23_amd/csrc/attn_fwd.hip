@@ -61,11 +61,12 @@ struct FwdCfg {
   static constexpr int STAGE = 2 * BC * D;   // one slot: a K tile then a V tile, row-major
 };
 
-// Lazy rescaling threshold (log2 units).  The running reference max m of a row
-// is raised only when a tile's max exceeds it by more than this, so most
-// tiles skip the O-accumulator rescale.  p = exp2(s*c - m) then stays below
-// 2^kTau; the result is unchanged (the same m is used for O and l).
+// Lazy rescaling bound (log2 units).  The running reference max m of a row
+// is raised only when some p = exp2(s*c - m) of a tile would exceed 2^kTau,
+// so most tiles skip the O-accumulator rescale; the result is unchanged (the
+// same m is used for O and l).
 constexpr float kTau = 8.0f;
+constexpr float kTauPow = 256.0f;  // 2^kTau
 
 // Longest sequence (d = 64, no block mask, no dropout) that the forward runs
 // with the one-tile-at-a-time kernel: up to eight 64-key tiles per workgroup.
@@ -224,46 +225,62 @@ __device__ __forceinline__ void fwd_bf16_item(const bf16* __restrict__ Q, const 
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
     return pair_max(mx) * c;
   };
-  // raise the reference max when the tile's max passed it by more than kTau
-  auto rescale = [&](float mt) {
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+  // raise the reference max to the tile's max (a no-op where the tile's max
+  // is not above it), rescaling l and the O accumulators
+  auto raise_max = [&](float mt) {
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
+    for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-    }
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
   };
-  // p = exp2(s c - m) in place, the row sum into l, and the P^T operands.
-  // With dropout, l sums every p (L is the logsumexp without dropout) and the
-  // dropped entries become 0 in the P V operand; 1 / (1 - rate) is applied
-  // with the division by l at the end.
-  auto exps = [&](f32x16 (&st)[2], bf16x8 (&pop)[4], int kv0) {
+  // p = exp2(s c - m) into the P^T operands (the scores stay), and this
+  // lane's sum of p into rs.  With dropout, rs sums every p (L is the
+  // logsumexp without dropout) and the dropped entries become 0 in the P V
+  // operand; 1 / (1 - rate) is applied with the division by l at the end.
+  auto exps = [&](const f32x16 (&st)[2], bf16x8 (&pop)[4], int kv0, float& rs) {
     const float mneg = -m_run;
-    float rs = 0.f;
+    f32x16 p[2];
+    rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(st[kb][r], c, mneg));
-        st[kb][r] = p;
-        rs += p;
+        p[kb][r] = fast_exp2(fmaf(st[kb][r], c, mneg));
+        rs += p[kb][r];
       }
-    l_run += rs;
     if constexpr (DROP) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         uint32_t word[4];
         drop_words_row(q, kv0 + 32 * kb, g, bh, seed_lo, seed_hi, word);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st[kb][r] = drop_keep(word, r, drop_t) ? st[kb][r] : 0.f;
+        for (int r = 0; r < 16; ++r) p[kb][r] = drop_keep(word, r, drop_t) ? p[kb][r] : 0.f;
       }
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) pop[m] = c_to_operand(st[m >> 1], m & 1);
+    for (int m = 0; m < 4; ++m) {
+      pop[m] = c_to_operand(p[m >> 1], m & 1);
+      // formed here, not sunk past the check below, so p is dead before it
+      asm volatile("" : "+v"(pop[m]));
+    }
+  };
+  // Lazy rescaling without a tile max on the common path.  Every p of a lane
+  // is at most that lane's sum, so a sum of at most 2^kTau shows that the
+  // reference max may stay.  Otherwise (a p above 2^kTau, or an inf or NaN
+  // sum) the tile's max is formed, m raised to it, and p recomputed; the
+  // scores are still in registers for that.  Either way every p is at most
+  // 2^kTau, and m changes only through raise_max, so O and l stay on one
+  // reference.
+  auto check_exps = [&](const f32x16 (&st)[2], bf16x8 (&pop)[4], int kv0, float& rs) {
+    if (__builtin_amdgcn_ballot_w64(!(rs <= kTauPow)) != 0) {
+      raise_max(tile_max(st));
+      exps(st, pop, kv0, rs);
+    }
+    l_run += rs;
   };
   // O^T += V^T P^T for the V tile in `slot`
   auto pv = [&](int slot, const bf16x8 (&pop)[4]) {
@@ -322,10 +339,15 @@ __device__ __forceinline__ void fwd_bf16_item(const bf16* __restrict__ Q, const 
       if (j < wave_tiles) {
         f32x16 st[2];
         bf16x8 pop[4];
+        // (the tile max first here: keeping the scores live through the
+        // exponentials would take this kernel past 128 VGPRs)
+        float rs;
         scores(slot, st);
         if (needs_mask(kv0)) mask(st, kv0);
-        rescale(tile_max(st));
-        exps(st, pop, kv0);
+        const float mt = tile_max(st);
+        if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) raise_max(mt);
+        exps(st, pop, kv0, rs);
+        l_run += rs;
         pv(slot, pop);
       }
       wait_vmem_all();  // tile j+1 has landed; every wave is done with slot j & 1
@@ -350,7 +372,7 @@ __device__ __forceinline__ void fwd_bf16_item(const bf16* __restrict__ Q, const 
     if (wave_tiles > 0) {
       scores(0, sa);
       if (needs_mask(kv_first)) mask(sa, kv_first);
-      rescale(tile_max(sa));
+      m_run = fmaxf(m_run, tile_max(sa));  // (l and O are still 0)
     }
     // first keys of tiles j+1 and j+2 at the start of step j, carried from step
     // to step; a block-sparse step reads the entry for j+3 from the LDS list
@@ -372,16 +394,14 @@ __device__ __forceinline__ void fwd_bf16_item(const bf16* __restrict__ Q, const 
         // its keys lies past this wave's rows or past N, so the mask sets them
         // all to -inf, and the rescale is skipped.  One code path per step.
         bf16x8 pop[4];
+        float rs;
         scores(par ^ 1, nxt);
-        exps(cur, pop, j * C::BC);  // (dropout runs on dense tiles only, so tile j starts at key 64 j)
-        pv(par, pop);
+        exps(cur, pop, j * C::BC, rs);  // (dropout runs on dense tiles only, so tile j starts at key 64 j)
         pin_a();
+        check_exps(cur, pop, j * C::BC, rs);
+        pv(par, pop);
         pin_b();
-        // Without a use here the compiler sinks the row sum's adds past the
-        // mask branch, out of the block where they overlap the MFMAs.
-        asm volatile("" ::"v"(l_run));
         if (needs_mask(kv_a)) mask(nxt, kv_a);
-        if (j + 1 < wave_tiles) rescale(tile_max(nxt));
       }
       wait_vmem_all();  // K(j+2) and V(j+1) have landed in LDS
       __syncthreads();

@@ -160,26 +160,34 @@ def test_scale_sign_decode(attn, scale):
 # ---------------------------------------------------------------- the lazy rescale
 def _ramp_inputs(N, d, scale, climb, causal, seed):
     """Scores that rise by `climb` log2 units per 64 keys: q_i = t e_0 and
-    k_j = (j / 64) e_0 plus small N(0, 0.1^2) noise in the other columns, with
-    t = climb / (scale log2 e), both rounded to bf16 like every input.
-    (The large factor sits in Q: dQ uses delta~ = rowsum(dO * O) over the
-    stored bf16 O, whose rounding error is multiplied by sum_j P_ij K_j, so
-    keys of magnitude ~N would test that reading instead of the rescale.)"""
+    k_j = (5 j / N) e_0 plus small N(0, 0.1^2) noise in the other columns, with
+    t = climb N / (5 * 64 * scale log2 e), both rounded to bf16 like every input.
+    (The large factor sits in Q and the keys stay below 5 at any N: dQ uses
+    delta~ = rowsum(dO * O) over the stored bf16 O, whose rounding error is
+    multiplied by sum_j P_ij K_j, so larger keys would test that reading
+    instead of the rescale.)"""
     g = torch.Generator().manual_seed(seed)
-    t = climb / (scale * math.log2(math.e))
+    t = climb * N / (5 * 64 * scale * math.log2(math.e))
     q = 0.1 * torch.randn(1, 2, N, d, generator=g)
     k = 0.1 * torch.randn(1, 2, N, d, generator=g)
     v = torch.randn(1, 2, N, d, generator=g)
     do = torch.randn(1, 2, N, d, generator=g)
     q[..., 0] = t
-    k[..., 0] = torch.arange(N, dtype=torch.float32) / 64.0
+    k[..., 0] = torch.arange(N, dtype=torch.float32) * (5.0 / N)
     return {n: x.to(torch.bfloat16) for n, x in (("q", q), ("k", k), ("v", v), ("do", do))}
 
 
-@pytest.mark.parametrize("climb", [7.9, 8.1])
-@pytest.mark.parametrize("d,causal", [(64, True), (64, False), (128, True), (128, False)])
-def test_lazy_rescale_climbing_scores(attn, climb, d, causal):
-    N = 333  # five 64-key tiles and a ragged tail
+# The short d=64 forward (N <= 512) raises m when a tile's max passes it by
+# more than 8 (log2 units); the other forwards when some p of a lane would
+# pass 2^8, found from the lane's row sum.  Climbs just below and above 8 per
+# tile drive the first rule to both sides of its threshold; the second rule
+# takes the slow path on most tiles at those climbs and, at 3 per tile, only
+# once the scores have risen 8 above the reference max.
+@pytest.mark.parametrize("climb", [3.0, 7.9, 8.1])
+@pytest.mark.parametrize("d,causal,N", [(64, True, 333), (64, False, 333), (128, True, 333), (128, False, 333),
+                                        (64, True, 700), (64, False, 700)])
+def test_lazy_rescale_climbing_scores(attn, climb, d, causal, N):
+    # N = 333: five 64-key tiles and a ragged tail; 700: past the short d=64 forward
     scale = 1 / math.sqrt(d)
     inp = _ramp_inputs(N, d, scale, climb, causal, seed=int(10 * climb) + d + causal)
     _say(f"ramp climb={climb}/tile d={d} causal={causal}")
