@@ -11,8 +11,8 @@
 //   used here.
 //
 // bf16 kernel design (MI355X, CDNA4):
-//   * One workgroup = 4 waves = 128 query rows, 32 per wave; two workgroups
-//     share a CU (224 VGPRs, two waves per SIMD).
+//   * One workgroup = 4 waves = 128 query rows, 32 per wave; at d = 128 two
+//     workgroups share a CU (up to 256 VGPRs, two waves per SIMD).
 //   * Software pipeline inside each wave: the scores of tile j+1 are formed
 //     while tile j's exponentials run, then tile j's P V, all in one basic
 //     block whose instruction order is pinned (sched_group_barrier), so the
@@ -26,8 +26,9 @@
 //     LDS reads (ds_read_b64_tr_b16), so V needs no transpose on the way in.
 //   * Softmax in base 2: p = exp2(s * scale * log2(e) - m) with one FMA and one
 //     v_exp_f32 per score; L = (m + log2 l) ln 2 at the end.  The reference max
-//     m moves only when a tile's max exceeds it by more than 2^8 (lazy
-//     rescaling), so the O accumulators are rarely touched by the VALU.
+//     m moves only when some p of a tile would exceed 2^8 (lazy rescaling), so
+//     the O accumulators are rarely touched by the VALU.  Each lane's row sum
+//     of p shows whether that happened, so the tile max is formed only then.
 //   * Global loads use raw buffer resources: per-lane offsets are
 //     loop-invariant, the tile offset is a scalar, rows past N read as zero.
 //   * K/V tiles of 64 keys are double-buffered in LDS and loaded by buffer ->
@@ -38,10 +39,13 @@
 //     skips the tiles past its own last row; only diagonal (and ragged tail)
 //     tiles apply the mask.  Query tiles run longest first within a head, and
 //     work items are renumbered so each XCD sweeps whole heads (L2 reuse).
-//   * Short sequences at d = 64 (N <= 512, a few tiles per workgroup) take a
-//     variant without the in-wave pipeline: one score tile in registers, 122
-//     VGPRs, four workgroups per CU, so more workgroups have loads in flight
-//     in a regime where HBM latency, not the matrix cores, sets the time.
+//   * At d = 64 the non-causal forward (any length) and the causal one up to
+//     N = 512 take a variant without the in-wave pipeline: one score tile in
+//     registers, under 128 VGPRs, four workgroups per CU.  Short sequences
+//     are HBM-latency bound, and more workgroups keep more loads in flight;
+//     long ones are bound by the VALU softmax (at d = 64 a tile's exponentials
+//     take more VALU cycles than its matrix products take MFMA cycles), and
+//     four waves per SIMD keep that pipe busier than three pipelined ones.
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -68,9 +72,15 @@ struct FwdCfg {
 constexpr float kTau = 8.0f;
 constexpr float kTauPow = 256.0f;  // 2^kTau
 
-// Longest sequence (d = 64, no block mask, no dropout) that the forward runs
-// with the one-tile-at-a-time kernel: up to eight 64-key tiles per workgroup.
+// Longest causal sequence (d = 64, no block mask, no dropout) that the
+// forward runs with the one-tile-at-a-time kernel: up to eight 64-key tiles
+// per workgroup (the non-causal d = 64 forward takes it at every length).
 constexpr int kShortSeqMaxN = 512;
+
+// Fewest tiles per workgroup for which the one-tile loop lowers a wave's
+// priority as it progresses (measured: 3-5% faster from 16 tiles up, 20%
+// slower at 4).
+constexpr int kPrioMinTiles = 16;
 
 // One work item (query tile qt of head bh, work = bh * n_qtiles + index) of
 // the forward, by one workgroup of 256 threads.
@@ -330,6 +340,18 @@ __device__ __forceinline__ void fwd_bf16_item(const bf16* __restrict__ Q, const 
     wait_vmem_all();
     __syncthreads();
     for (int j = 0; j < n_tiles; ++j) {
+      // The four waves of a SIMD come from four workgroups, and the hardware
+      // issues oldest first, so the first workgroup runs ahead and the CU
+      // ends with one wave left.  On long loops a wave lowers its own
+      // priority as it passes each quarter of its tiles, so waves that are
+      // behind get the issue slots.
+      if (n_tiles >= kPrioMinTiles) {
+        const int band = (4 * j) / n_tiles;
+        if (band == 0) __builtin_amdgcn_s_setprio(3);
+        else if (band == 1) __builtin_amdgcn_s_setprio(2);
+        else if (band == 2) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
       const int slot = j & 1;
       const int kv0 = kv0_of(j);
       if (j + 1 < n_tiles) {
@@ -339,14 +361,20 @@ __device__ __forceinline__ void fwd_bf16_item(const bf16* __restrict__ Q, const 
       if (j < wave_tiles) {
         f32x16 st[2];
         bf16x8 pop[4];
-        // (the tile max first here: keeping the scores live through the
-        // exponentials would take this kernel past 128 VGPRs)
+        // The scores die as p is formed (this kernel stays under 128 VGPRs);
+        // the rare slow path forms them again from the K tile, which stays in
+        // its slot until the barrier below.
         float rs;
         scores(slot, st);
         if (needs_mask(kv0)) mask(st, kv0);
-        const float mt = tile_max(st);
-        if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau) != 0) raise_max(mt);
+        if (j == 0) m_run = fmaxf(m_run, tile_max(st));  // (l and O are still 0)
         exps(st, pop, kv0, rs);
+        if (__builtin_amdgcn_ballot_w64(!(rs <= kTauPow)) != 0) {
+          scores(slot, st);
+          if (needs_mask(kv0)) mask(st, kv0);
+          raise_max(tile_max(st));
+          exps(st, pop, kv0, rs);
+        }
         l_run += rs;
         pv(slot, pop);
       }
@@ -561,7 +589,7 @@ hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* 
   // (at d = 128 the pipelined kernel's state already limits a CU to two
   // workgroups by LDS as well as registers)
   constexpr bool kShortFwd = D == 64;
-  const bool short_seq = kShortFwd && N <= kShortSeqMaxN;
+  const bool short_seq = kShortFwd && (!CAUSAL || N <= kShortSeqMaxN);
   const ScoreScale sc = split_scale(scale);
   if (m.ptr)
     hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, true, false>), dim3(total), dim3(256), 0, stream,

@@ -96,8 +96,10 @@ SMALL = [
     (1, 2, 1, 64, False), (1, 2, 1, 128, True), (1, 2, 17, 64, True), (2, 3, 200, 64, False),
     (1, 2, 333, 128, True), (1, 2, 512, 128, False), (2, 2, 1000, 128, True), (1, 3, 257, 64, True),
     (1, 2, 640, 64, False), (1, 1, 129, 128, False), (1, 2, 1100, 64, True),
-    # the last length the one-tile-at-a-time d=64 forward takes, and the first past it
-    (1, 2, 512, 64, True), (1, 2, 513, 64, False),
+    # the last causal length the one-tile-at-a-time d=64 forward takes, and the
+    # first past it; non-causal d=64 takes it at every length, lowering wave
+    # priority by quarters from 16 tiles on (ragged last tile)
+    (1, 2, 512, 64, True), (1, 2, 513, 64, True), (1, 2, 513, 64, False), (1, 2, 1100, 64, False),
     # causal with B*H a multiple of 8 and an even number of 128-row tiles: the
     # forward and the dq kernel run two query tiles per workgroup (ragged last tile)
     (1, 8, 1000, 128, True), (2, 4, 900, 64, True),
