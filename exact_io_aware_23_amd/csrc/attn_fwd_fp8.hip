@@ -22,7 +22,8 @@
 //     transposing byte reads (ds_read_b64_tr_b8).  dv is applied with the
 //     final division by l.
 //   * The probabilities are p = 2^(s - m) with a lazily raised reference max
-//     m (raised only when a tile's max passes it by more than 2^8), so
+//     m (raised only when some p of a tile would pass 2^8, which each lane's
+//     row sum of p shows, so no tile max is formed on the common path), so
 //     p <= 256 stays inside the e4m3 range; l sums the unrounded p in fp32.
 //   * Everything else is the bf16 kernel's: 4 waves x 32 query rows, 64-key
 //     K/V tiles double-buffered in LDS through buffer -> LDS copies, one
@@ -86,7 +87,7 @@ __device__ __forceinline__ i32x2 lds_tr8(const uint8_t* p) {
 }
 __device__ __forceinline__ i32x4 lds16b(const uint8_t* p) { return *reinterpret_cast<const i32x4*>(p); }
 
-constexpr float kTau8 = 8.0f;  // lazy rescaling threshold (log2 units); also keeps p <= 2^8
+constexpr float kTau8Pow = 256.0f;  // lazy rescaling bound 2^8: every p <= 2^8 (fits e4m3)
 
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(256, 2)
@@ -219,42 +220,55 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][r]);
     return pair_max(mx) * c;
   };
-  auto rescale = [&](float mt) {
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kTau8) != 0) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+  // raise the reference max to the tile's max (a no-op where it is not
+  // above it), rescaling l and the O accumulators
+  auto raise_max = [&](float mt) {
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
+    for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-    }
+      for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
   };
-  // p = 2^(s c - m), the row sum into l, and P^T as e4m3 bytes: byte e of
-  // the operand is register e % 16 of half e / 16 (key 32 (e/16) + crow)
-  auto exps = [&](f32x16 (&st)[2], i32x8& pop) {
+  // p = 2^(s c - m) (the scores stay), this lane's sum of p into rs, and P^T
+  // as e4m3 bytes: byte e of the operand is register e % 16 of half e / 16
+  // (key 32 (e/16) + crow)
+  auto exps = [&](const f32x16 (&st)[2], i32x8& pop, float& rs) {
     const float mneg = -m_run;
-    float rs = 0.f;
+    f32x16 p[2];
+    rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(st[kb][r], c, mneg));
-        st[kb][r] = p;
-        rs += p;
+        p[kb][r] = fast_exp2(fmaf(st[kb][r], c, mneg));
+        rs += p[kb][r];
       }
-    l_run += rs;
     // (the first conversion of a word writes its low half and keeps the high
     // half of its third operand, which the second overwrites: passing a
     // register that dies there instead of 0 saves a v_mov per word)
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int kb = w >> 2, r = 4 * (w & 3);
-      int x = __builtin_amdgcn_cvt_pk_fp8_f32(st[kb][r], st[kb][r + 1], __builtin_bit_cast(int, st[kb][r]), false);
-      x = __builtin_amdgcn_cvt_pk_fp8_f32(st[kb][r + 2], st[kb][r + 3], x, true);
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(p[kb][r], p[kb][r + 1], __builtin_bit_cast(int, p[kb][r]), false);
+      x = __builtin_amdgcn_cvt_pk_fp8_f32(p[kb][r + 2], p[kb][r + 3], x, true);
       pop[w] = x;
     }
+    // formed here, not sunk past the check below
+    asm volatile("" : "+v"(pop));
+  };
+  // The lazy rescale without a tile max on the common path (as in the bf16
+  // forward): a lane's sum of p bounds every p it holds, so a sum of at most
+  // 2^kTau8 lets m stay (p then fits e4m3); otherwise, or on inf / NaN, the
+  // tile's max is formed, m raised to it, and p formed again from the scores.
+  auto check_exps = [&](const f32x16 (&st)[2], i32x8& pop, float& rs) {
+    if (__builtin_amdgcn_ballot_w64(!(rs <= kTau8Pow)) != 0) {
+      raise_max(tile_max(st));
+      exps(st, pop, rs);
+    }
+    l_run += rs;
   };
   auto pv = [&](int slot, const i32x8& pop) {
     const uint8_t* Vs = smem + slot * C::STAGE + C::TILE;
@@ -300,7 +314,7 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
   if (wave_tiles > 0) {
     scores(0, sa);
     if (needs_mask(0)) mask(sa, 0);
-    rescale(tile_max(sa));
+    m_run = fmaxf(m_run, tile_max(sa));  // (l and O are still 0)
   }
   __syncthreads();  // every wave has read K(0) before K(2) is loaded over it
 
@@ -319,16 +333,15 @@ fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, con
       // the scores of tile j+1 are formed even when this wave has no such
       // tile (the slot holds an in-bounds K tile whose keys the mask removes)
       i32x8 pop;
+      float rs;
       scores(par ^ 1, nxt);
-      exps(cur, pop);
-      pv(par, pop);
+      exps(cur, pop, rs);
       pin_a();
+      check_exps(cur, pop, rs);
+      pv(par, pop);
       pin_b();
       if constexpr (MASKED) {
         if (needs_mask(kv_a)) mask(nxt, kv_a);
-        if (j + 1 < wave_tiles) rescale(tile_max(nxt));
-      } else {
-        rescale(tile_max(nxt));
       }
     }
     wait_vmem_all();

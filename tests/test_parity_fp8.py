@@ -120,6 +120,39 @@ def test_fp8_sharp_softmax(attn):
         check_fp8(f"sharp h={h}", o[0, h], lse[0, h], *heads_ref(inp, 0, h, scale, False))
 
 
+def _quantize_e4m3(x):
+    """fp32 tensor -> (e4m3 codes, descale) with the recipe of the workload
+    generator: the largest magnitude maps to 448."""
+    amax = float(x.abs().max())
+    descale = float(torch.tensor(max(amax, 1e-30) / 448.0, dtype=torch.float32))
+    return (x / descale).to(torch.float8_e4m3fn).view(torch.uint8), descale
+
+
+@pytest.mark.parametrize("climb", [3.0, 8.1])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_lazy_rescale_climbing_scores(attn, climb, causal):
+    """Scores that rise by about `climb` log2 units per 64-key tile (q_i = t e_0,
+    k_j = (5 j / N) e_0 plus N(0, 0.1^2) noise elsewhere), so the reference max
+    is raised along the row: the slow path (tile max, rescale, exponentials
+    again) runs on most tiles at 8.1 and once the scores have climbed 8 at 3."""
+    B, H, N, d = 1, 2, 700, 128
+    scale = 1 / math.sqrt(d)
+    g = torch.Generator().manual_seed(int(10 * climb) + causal)
+    t = climb * N / (5 * 64 * scale * math.log2(math.e))
+    q = 0.1 * torch.randn(B, H, N, d, generator=g)
+    k = 0.1 * torch.randn(B, H, N, d, generator=g)
+    v = torch.randn(B, H, N, d, generator=g)
+    q[..., 0] = t
+    k[..., 0] = torch.arange(N, dtype=torch.float32) * (5.0 / N)
+    inp = {}
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        inp[name + "8"], inp["d" + name] = _quantize_e4m3(x)
+    _say(f"fp8 ramp climb={climb} causal={causal}")
+    o, lse = run(attn, inp, scale, causal)
+    for h in range(H):
+        check_fp8(f"ramp {climb} c={causal} h={h}", o[0, h], lse[0, h], *heads_ref(inp, 0, h, scale, causal))
+
+
 def test_fp8_descales_enter_as_stated(attn):
     """Halving dq and doubling scale gives the same S, so the same O and L bit
     for bit; doubling dv doubles O exactly (a power of two)."""
