@@ -118,7 +118,9 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int dt, int h, co
   return out;
 }
 
-template <int D, bool CAUSAL, bool SPARSE, bool DROP>
+// PAIR: each workgroup runs two key blocks of one head, p and n - 1 - p
+// (pair_work), so causal workgroups all do the same work.
+template <int D, bool CAUSAL, bool SPARSE, bool DROP, bool PAIR = false>
 __global__ void __launch_bounds__(256, 2)
 bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                 const float* __restrict__ Lse, const bf16* __restrict__ dO, const float* __restrict__ Delta,
@@ -135,7 +137,9 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   bf16* Xs = Vs + C::V_ELEMS;                                          // stage s: Q at s*STAGE, dO after
   float* Fs = reinterpret_cast<float*>(smem + (C::V_ELEMS + 2 * C::STAGE) * 2);  // stage s: L' [32], delta [32]
 
-  const int work = xcd_remap(blockIdx.x, total);
+#pragma nounroll
+  for (int item = 0; item < (PAIR ? 2 : 1); ++item) {
+  const int work = PAIR ? pair_work(blockIdx.x, total, n_ktiles, item) : xcd_remap(blockIdx.x, total);
   const int bh = work / n_ktiles;
   const int kt = work % n_ktiles;
   const size_t head = (size_t)bh * N * D;
@@ -396,6 +400,8 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
         *reinterpret_cast<u32x2*>(dVh + dcol) = wv;
       }
   }
+  if (PAIR) __syncthreads();  // every wave is done with this block's LDS before the next block's copies
+  }
 }
 
 // ------------------------------------------------------------------ dQ
@@ -652,9 +658,11 @@ bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16
 
 // Longest causal sequence, in 128-row query tiles, whose dq kernel runs two
 // tiles per workgroup (measured: dq 1.3% faster at 64 tiles and 0.6% slower
-// at 256; the same pairing made dkdv 0.5% slower at 64 tiles, where its
-// two-block loop spills registers, so dkdv keeps one key block per workgroup).
+// at 256).
 constexpr int kBwdPairMaxTiles = 64;
+// The same for dkdv, in 128-key blocks.  Its two-block loop spills 10 VGPRs
+// (d = 128): 8% faster at 32 blocks, 0.5% slower at 64.
+constexpr int kDkdvPairMaxTiles = 32;
 
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const float* lse, const void* dout,
@@ -674,6 +682,10 @@ hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const floa
   else if (dr.on)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false, true>), ATTN_DKDV_ARGS, (const uint8_t*)nullptr, 0, 0,
                        dr.t, dr.seed_lo, dr.seed_hi, dr.inv_keep, sc.mode);
+  else if (CAUSAL && BH % 8 == 0 && n_kt % 2 == 0 && n_kt <= kDkdvPairMaxTiles)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false, false, true>), dim3(total / 2), dim3(256), 0, stream,
+                       (const bf16*)q, (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dk,
+                       (bf16*)dv, N, n_kt, total, sc.c, scale, (const uint8_t*)nullptr, 0, 0, 0u, 0u, 0u, 1.f, sc.mode);
   else
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false, false>), ATTN_DKDV_ARGS, (const uint8_t*)nullptr, 0, 0,
                        0u, 0u, 0u, 1.f, sc.mode);

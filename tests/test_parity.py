@@ -101,7 +101,8 @@ SMALL = [
     # priority by quarters from 16 tiles on (ragged last tile)
     (1, 2, 512, 64, True), (1, 2, 513, 64, True), (1, 2, 513, 64, False), (1, 2, 1100, 64, False),
     # causal with B*H a multiple of 8 and an even number of 128-row tiles: the
-    # forward and the dq kernel run two query tiles per workgroup (ragged last tile)
+    # forward and the dq kernel run two query tiles per workgroup, dkdv two key
+    # blocks (ragged last tile)
     (1, 8, 1000, 128, True), (2, 4, 900, 64, True),
 ]
 
