@@ -75,6 +75,9 @@ def parse():
                     help="after the timed steps, repeat the step this long while sampling the GPU clock (0: skip)")
     ap.add_argument("--dropout", type=float, default=None, help="time the dropout entry points at this rate")
     ap.add_argument("--fp8", action="store_true", help="time attn_fwd_fp8 (e4m3 inputs) on the workload's shape")
+    ap.add_argument("--probe", action="store_true",
+                    help="run the hardware probes of include/attn_probe.h (LDS, issue rates, wave placement, "
+                         "atomics, exp2 accuracy) and print their rates")
     ap.add_argument("--decode", type=int, default=None, help="time attn_decode with this many queries per head")
     ap.add_argument("--decode-nk", type=int, default=16384, help="cached keys per head for --decode")
     ap.add_argument("--flush-l2", action="store_true",
@@ -292,6 +295,107 @@ def copy_calibration(args):
     print(json.dumps({"metric": "device copy GB/s (counter calibration)", "value": round(2 * COPY_BYTES / dt / 1e9, 1),
                       "unit": "GB/s", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES, "steps": args.steps}),
           flush=True)
+    return 0
+
+
+def bench_probe(args):
+    """The hardware probes of include/attn_probe.h; prints one JSON line with
+    the rates the design quotes (each probe's kernel is described in that
+    header)."""
+    import numpy as np
+
+    from exact_io_aware_23_amd import binding
+
+    lib = binding.load_library()
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream(dev)
+    st = stream.cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    P = lambda t: t.data_ptr()
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    out = {"metric": "hardware probes (include/attn_probe.h)", "cus": cus}
+    # LDS read throughput: per CU (from each workgroup's own cycle count, the
+    # workgroups of a CU running together) and over the whole chip (events)
+    lds = {}
+    for mode, name, nbytes in ((0, "ds_read_b128", 16), (1, "ds_read_b64_tr_b16", 8)):
+        for per_cu in (1, 2, 4):
+            wgs = cus * per_cu
+            sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+            cyc = torch.empty(wgs, dtype=torch.int64, device=dev)
+
+            def run():
+                assert lib.attn_probe_lds_rate(mode, wgs, P(sink), P(cyc), st) == 0
+
+            ms = timed(run)
+            per_wg = 256 * 2048 * 8 * nbytes
+            mean_cyc = float(cyc.double().mean())
+            lds[f"{name} x{per_cu}/CU"] = {"bytes_per_clk_per_cu": round(per_wg * per_cu / mean_cyc, 1),
+                                           "tb_per_s": round(per_wg * wgs / (ms * 1e-3) / 1e12, 1)}
+    out["lds_read"] = lds
+    # issue rates: cycles per instruction of each wave; waves w and w+4 share a SIMD
+    cases = [("exp, one wave per SIMD", [1] * 4), ("fma, one wave per SIMD", [2] * 4), ("mfma, one wave per SIMD", [3] * 4),
+             ("exp + exp", [1] * 8), ("mfma + exp", [3] * 4 + [1] * 4), ("mfma + fma", [3] * 4 + [2] * 4),
+             ("exp + fma", [1] * 4 + [2] * 4)]
+    issue = {}
+    for name, kinds in cases:
+        k = torch.tensor(kinds, dtype=torch.int32, device=dev)
+        nw = len(kinds)
+        sink = torch.empty(cus * 64 * nw, dtype=torch.float32, device=dev)
+        cyc = torch.zeros(cus * 8, dtype=torch.int64, device=dev)
+        assert lib.attn_probe_issue(P(k), nw, cus, P(sink), P(cyc), st) == 0
+        torch.cuda.synchronize()
+        assert lib.attn_probe_issue(P(k), nw, cus, P(sink), P(cyc), st) == 0
+        torch.cuda.synchronize()
+        c = cyc.view(cus, 8)[:, :nw].double().mean(0).tolist()
+        names = {1: "exp", 2: "fma", 3: "mfma"}
+        per = {}
+        for grp, lo in (("waves 0-3", 0), ("waves 4-7", 4)):
+            if lo >= nw:
+                continue
+            kind = kinds[lo]
+            n_inst = 4096 if kind == 3 else 8 * 4096
+            per[f"{grp} ({names[kind]})"] = round(sum(c[lo:lo + 4]) / 4 / n_inst, 2)
+        issue[name] = per
+    out["issue_cycles_per_instruction"] = issue
+    # wave placement of 8-wave workgroups
+    hw = torch.empty(512 * 8, dtype=torch.int32, device=dev)
+    assert lib.attn_probe_wave_simd(512, P(hw), st) == 0
+    torch.cuda.synchronize()
+    h = hw.view(512, 8).cpu().to(torch.int64)
+    simd, cu = (h >> 4) & 3, (h >> 8) & 0xF
+    same = ((simd[:, :4] == simd[:, 4:]) & (cu[:, :4] == cu[:, 4:])).double().mean().item()
+    out["waves_w_and_w+4_share_a_simd"] = round(same, 4)
+    # global fp32 updates: atomics against a plain load-add-store, 4 bytes per element
+    atom = {}
+    for mib in (4, 64, 256):
+        n = mib * (1 << 20) // 4
+        t = torch.zeros(n, dtype=torch.float32, device=dev)
+        for mode, name in ((1, "atomic_add_f32"), (0, "load_add_store")):
+            ms = timed(lambda: lib.attn_probe_atomic(P(t), n, mode, st))
+            atom[f"{name} {mib} MiB"] = round(n * 4 / (ms * 1e-3) / 1e9, 1)
+    out["global_update_gb_per_s"] = atom
+    # v_exp_f32 against exact exp2 (fp64), in float32 ulps of the exact value
+    x = torch.linspace(-39.5, 0.5, 1 << 22, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    assert lib.attn_probe_exp2(P(x), P(y), x.numel(), st) == 0
+    torch.cuda.synchronize()
+    xs, ys = x.cpu().double().numpy(), y.cpu().double().numpy()
+    ref = np.exp2(xs)
+    ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
+    out["v_exp_f32_max_ulp_on_-39.5_0.5"] = round(float(np.max(np.abs(ys - ref) / ulp)), 3)
+    out["host"] = host_facts()
+    print(json.dumps(out), flush=True)
     return 0
 
 
@@ -652,6 +756,8 @@ def main():
         return 1
     if args.which == "copy":
         return copy_calibration(args)
+    if args.probe:
+        return bench_probe(args)
     import exact_io_aware_23_amd as A
 
     A.load_library()

@@ -44,6 +44,12 @@ _SIGNATURES = {
     "attn_fwd_fp8": (_I, [_P, _P, _P, _F, _F, _F, _P, _P, _I, _I, _I, _I, _F, _I, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
     "attn_abi_version": (_I, []),
+    # hardware probes (include/attn_probe.h)
+    "attn_probe_lds_rate": (_I, [_I, _I, _P, _P, _P]),
+    "attn_probe_issue": (_I, [_P, _I, _I, _P, _P, _P]),
+    "attn_probe_wave_simd": (_I, [_I, _P, _P]),
+    "attn_probe_atomic": (_I, [_P, _S, _I, _P]),
+    "attn_probe_exp2": (_I, [_P, _P, _S, _P]),
 }
 
 

@@ -11,6 +11,7 @@ from exact_io_aware_23_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "attn_probe.h")
 
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: validation fails first
 
@@ -24,8 +25,8 @@ def lib():
     return binding.load_library()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
 
@@ -38,13 +39,32 @@ def test_header_declares_the_expected_entry_points():
         "attn_decode", "attn_fwd_fp8", "attn_bwd_noalloc", "attn_bwd_noalloc_max_rows"])
 
 
+def test_probe_header_declares_the_probes():
+    assert declared_functions(PROBE_HEADER) == sorted([
+        "attn_probe_lds_rate", "attn_probe_issue", "attn_probe_wave_simd", "attn_probe_atomic", "attn_probe_exp2"])
+
+
 def test_library_exports_every_declared_symbol(lib):
-    for name in declared_functions():
+    names = declared_functions() + declared_functions(PROBE_HEADER)
+    for name in names:
         assert hasattr(lib, name), name
     # and as plain C symbols (no C++ mangling)
     out = os.popen(f"nm -D --defined-only {binding.LIB_PATH}").read()
-    for name in declared_functions():
+    for name in names:
         assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_probe_validation(lib):
+    """Probes refuse out-of-range arguments with 1 before launching anything."""
+    assert lib.attn_probe_lds_rate(2, 4, FAKE, FAKE, None) == 1
+    assert lib.attn_probe_lds_rate(0, 0, FAKE, FAKE, None) == 1
+    assert lib.attn_probe_lds_rate(0, 4, None, FAKE, None) == 1
+    assert lib.attn_probe_issue(FAKE, 9, 4, FAKE, FAKE, None) == 1
+    assert lib.attn_probe_issue(FAKE, 4, 0, FAKE, FAKE, None) == 1
+    assert lib.attn_probe_wave_simd(0, FAKE, None) == 1
+    assert lib.attn_probe_atomic(FAKE, 100, 1, None) == 1  # not a multiple of 16384
+    assert lib.attn_probe_atomic(None, 16384, 1, None) == 1
+    assert lib.attn_probe_exp2(FAKE, FAKE, 0, None) == 1
 
 
 def test_abi_version_matches_header(lib):
