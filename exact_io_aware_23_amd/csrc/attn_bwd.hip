@@ -36,6 +36,7 @@
 // delta = sum_j P_ij dP_ij in fp32 from the same P and dP it forms, and dkdv
 // runs after it with that exact delta.  Order: preprocess -> dq -> dkdv.
 // Both recompute P with p = exp2(s * scale * log2 e - L * log2 e).
+#include <mutex>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -68,20 +69,29 @@ bwd_preprocess_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO, f
 }
 
 // ------------------------------------------------------------------ dK, dV
-template <int D>
+// QSPLIT: the four waves are two 32-key groups times two query halves (wave w
+// owns keys 32 (w % 2).. of the workgroup's 64 and the query block of parity
+// w / 2 in every 64-query step), and the two halves' partial dK, dV are added
+// through LDS at the end.  Each wave runs half as many steps and there are
+// twice as many waves, so a launch that would leave its last round of
+// workgroups one per SIMD splits more evenly.
+template <int D, bool QSPLIT = false>
 struct DkdvCfg {
-  static constexpr int BKV = 128;  // keys per workgroup, 32 per wave
-  static constexpr int BQ = 32;    // queries per step
+  static constexpr int KG = QSPLIT ? 2 : 4;          // key groups of 32 per workgroup
+  static constexpr int QH = QSPLIT ? 2 : 1;          // 32-query blocks per step, one per wave row
+  static constexpr int BKV = 32 * KG;                // keys per workgroup
+  static constexpr int BQ = 32;                      // queries per wave per step
   static constexpr int NCH = D / 8;
   static constexpr int KS = D / 16;
   static constexpr int DT = D / 32;
-  static constexpr int QTILE = BQ * D;               // bf16 elements of one Q or dO tile
+  static constexpr int QTILE = QH * BQ * D;          // bf16 elements of one step's Q (or dO) rows
   static constexpr int NB = QTILE * 2 / 1024 / 4;    // 1 KB transfers per wave per tile
   static constexpr int NBV = BKV * D * 2 / 1024 / 4; // 1 KB transfers per wave for the V block
-  // LDS (bf16 elements): V block [BKV][D] | 2 stages x (Q [BQ][D], dO [BQ][D]) | 2 stages x (L', D) fp32
+  // LDS (bf16 elements): V block [BKV][D] | 2 stages x (Q [QH BQ][D], dO [QH BQ][D]) | 2 stages x (L', D) fp32
   static constexpr int V_ELEMS = BKV * D;
   static constexpr int STAGE = 2 * QTILE;
-  static constexpr int BYTES = (V_ELEMS + 2 * STAGE) * 2 + 2 * 2 * BQ * 4;
+  static constexpr int NSTAT = 2 * QH * BQ;          // floats of statistics per stage
+  static constexpr int BYTES = (V_ELEMS + 2 * STAGE) * 2 + 2 * NSTAT * 4;
 };
 
 // A operand of a product contracting over rows of a row-major [rows][D] LDS
@@ -120,15 +130,16 @@ __device__ __forceinline__ bf16x8 tr_operand(const bf16* tile, int dt, int h, co
 
 // PAIR: each workgroup runs two key blocks of one head, p and n - 1 - p
 // (pair_work), so causal workgroups all do the same work.
-template <int D, bool CAUSAL, bool SPARSE, bool DROP, bool PAIR = false>
+template <int D, bool CAUSAL, bool SPARSE, bool DROP, bool PAIR = false, bool QSPLIT = false>
 __global__ void __launch_bounds__(256, 2)
 bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                 const float* __restrict__ Lse, const bf16* __restrict__ dO, const float* __restrict__ Delta,
                 bf16* __restrict__ dK, bf16* __restrict__ dV, int N, int n_ktiles, int total, float c,
                 float scale, const uint8_t* __restrict__ Mask, int mask_hs, int nb, uint32_t drop_t,
                 uint32_t seed_lo, uint32_t seed_hi, float inv_keep, uint32_t smode) {
-  using C = DkdvCfg<D>;
+  using C = DkdvCfg<D, QSPLIT>;
   static_assert(!(SPARSE && DROP), "block-sparse and dropout are separate entry points");
+  static_assert(!QSPLIT || (!SPARSE && !DROP && !PAIR), "the query split serves the dense kernel");
   __shared__ __attribute__((aligned(16))) char smem[C::BYTES];
   // block-sparse: the query blocks of this key block whose 128 x 128 block is on
   __shared__ uint16_t qlist[SPARSE ? kMaxSparseN / C::BQ : 1];
@@ -157,7 +168,8 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   const int l32 = lane & 31;
   const int g = lane >> 5;
   const int k0 = kt * C::BKV;
-  const int kw0 = k0 + 32 * wave;
+  const int kw0 = k0 + 32 * (wave % C::KG);
+  const int qh = QSPLIT ? wave / C::KG : 0;  // this wave's query block within a step
   const int key = kw0 + l32;
 
   // ---- K^T operand in VGPRs (lane = key, 8 consecutive d per k-step); V block into LDS
@@ -189,21 +201,22 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
       bload16_lds(rQ, Qs + b * 512, qoff[i], q0 * D * 2);
       bload16_lds(rdO, Qs + C::QTILE + b * 512, qoff[i], q0 * D * 2);
     }
-    if (tid < 32) {
+    constexpr int R = C::QH * C::BQ;  // query rows per step
+    if (tid < R) {
       // a row with no allowed key (L = -inf) gets p = exp2(-inf) = 0
       const float lrow = __uint_as_float(bload4(rL, (q0 + tid) * 4, 0));
       stat = lrow == -INFINITY ? INFINITY : lrow * kLog2e;
     }
-    else if (tid < 64) stat = __uint_as_float(bload4(rD, (q0 + tid - 32) * 4, 0));
+    else if (tid < 2 * R) stat = __uint_as_float(bload4(rD, (q0 + tid - R) * 4, 0));
   };
   auto store_stat = [&](int stage) {
-    if (tid < 64) Fs[stage * 64 + tid] = stat;
+    if (tid < C::NSTAT) Fs[stage * C::NSTAT + tid] = stat;
   };
 
   const int a_row = swap23(l32);
   const int a_swz = chunk_swz<C::NCH>(a_row);
   const TrBase<D> trb(lane);
-  const int v_row = 32 * wave + l32;
+  const int v_row = 32 * (wave % C::KG) + l32;
   const int v_swz = chunk_swz<C::NCH>(v_row);
 
   f32x16 dk[C::DT], dv[C::DT];
@@ -217,8 +230,9 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
 
   const int n_qt = (N + C::BQ - 1) / C::BQ;
   const int qt_begin = CAUSAL ? (k0 / C::BQ) : 0;
-  // the workgroup visits query blocks it_of(0), it_of(1), ... (n_it of them)
-  int n_it = max(n_qt - qt_begin, 0);
+  // the workgroup visits query blocks it_of(0), it_of(1), ... (n_it of them;
+  // with QSPLIT, steps of two blocks)
+  int n_it = max((n_qt - qt_begin + C::QH - 1) / C::QH, 0);
   if constexpr (SPARSE) {
     // query block t holds rows [32 t, 32 t + 32), in block row t / 4; this is block column kt
     const uint8_t* mcol = Mask + (size_t)bh * mask_hs + kt;
@@ -227,7 +241,7 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
   }
   auto it_of = [&](int idx) -> int {
     if constexpr (SPARSE) return uniform((int)qlist[idx]);
-    else return qt_begin + idx;
+    else return qt_begin + C::QH * idx;
   };
   // first rows of query blocks idx and idx+1, carried from iteration to
   // iteration; a block-sparse iteration reads the list entry for idx+2 early
@@ -243,16 +257,16 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     int raw2 = 0;
     if constexpr (SPARSE) raw2 = qlist[min(idx + 2, kMaxSparseN / C::BQ - 1)];
     const int stage = idx & 1;
-    const int q0 = q_cur;
+    const int q0 = q_cur + C::BQ * qh;  // this wave's query block
     const bool has_next = idx + 1 < n_it;
     if (has_next) load_q(q_nxt, stage ^ 1);
 
-    const bool active = kw0 < N && !(CAUSAL && q0 < kw0);
+    const bool active = kw0 < N && (!QSPLIT || q0 < N) && !(CAUSAL && q0 < kw0);
     if (active) {
-      const bf16* Qs = Xs + stage * C::STAGE;
+      const bf16* Qs = Xs + stage * C::STAGE + C::BQ * D * qh;
       const bf16* dOs = Qs + C::QTILE;
-      const float* Ls = Fs + stage * 64;
-      const float* Ds = Ls + 32;
+      const float* Ls = Fs + stage * C::NSTAT + C::BQ * qh;
+      const float* Ds = Ls + C::QH * C::BQ;
       // ---- S = Q K^T and dP = dO V^T
       // Each MFMA's operands are read one MFMA ahead; sched_barrier fences
       // the steps so the compiler cannot pull the reads down to their use.
@@ -379,11 +393,43 @@ bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf
     __syncthreads();
     q_cur = q_nxt;
     if constexpr (SPARSE) q_nxt = idx + 2 < n_it ? uniform(raw2) * C::BQ : 0;
-    else q_nxt = (qt_begin + idx + 2) * C::BQ;
+    else q_nxt = (qt_begin + C::QH * (idx + 2)) * C::BQ;
+  }
+
+  if constexpr (QSPLIT) {
+    // the second query half hands its partial dK, dV to the first through LDS
+    // (free after the loop's last barrier): chunk j of the 2 DT 4 float4s a lane
+    // holds goes to float4 slot (kg (2 DT 4) + j) 64 + lane, conflict-free
+    constexpr int NQ = 2 * C::DT * 4;
+    f32x4* xch = reinterpret_cast<f32x4*>(smem) + (wave % C::KG) * NQ * 64 + lane;
+    if (qh == 1) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          xch[(dt * 4 + a) * 64] = f32x4{dk[dt][4 * a], dk[dt][4 * a + 1], dk[dt][4 * a + 2], dk[dt][4 * a + 3]};
+          xch[((C::DT + dt) * 4 + a) * 64] =
+              f32x4{dv[dt][4 * a], dv[dt][4 * a + 1], dv[dt][4 * a + 2], dv[dt][4 * a + 3]};
+        }
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 pk = xch[(dt * 4 + a) * 64], pv = xch[((C::DT + dt) * 4 + a) * 64];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dk[dt][4 * a + e] += pk[e];
+            dv[dt][4 * a + e] += pv[e];
+          }
+        }
+    }
   }
 
   // ---- epilogue: dK = scale * (dK^T)^T, dV = (dV^T)^T
-  if (key < N) {
+  if (key < N && qh == 0) {
     bf16* dKh = dK + head + (size_t)key * D;
     bf16* dVh = dV + head + (size_t)key * D;
 #pragma unroll
@@ -664,6 +710,53 @@ constexpr int kBwdPairMaxTiles = 64;
 // (d = 128): 8% faster at 32 blocks, 0.5% slower at 64.
 constexpr int kDkdvPairMaxTiles = 32;
 
+// Resident workgroups of the unsplit dense non-causal d = 64 dkdv kernel on
+// the current GPU (the occupancy query times the CU count), looked up once per
+// device; 0 if unavailable.
+constexpr int kMaxDevicesBwd = 64;
+std::mutex g_dkdv_mu;
+int g_dkdv_slots[kMaxDevicesBwd] = {};
+
+int dkdv64_slots() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevicesBwd) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  std::lock_guard<std::mutex> lock(g_dkdv_mu);
+  if (g_dkdv_slots[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, (const void*)bwd_dkdv_kernel<64, false, false, false, false, false>, 256, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return 0;
+    }
+    g_dkdv_slots[dev] = per_cu > 0 && cus > 0 ? per_cu * cus : -1;
+  }
+  return g_dkdv_slots[dev];
+}
+
+// Whether dkdv runs with its query split (dense, d = 64, not causal: at d = 128
+// the split kernel would not fit two waves per SIMD).  The split doubles the
+// waves and the Q/dO copies; it pays when the unsplit launch takes few rounds
+// of resident workgroups and leaves its last round at most half full (then
+// that round runs one wave per SIMD): measured 6% faster at B=4 H=16 N=2048,
+// 18% on a few heads, 4% slower at N=8192 and where everything fits in one
+// round.
+template <int D, bool CAUSAL>
+bool dkdv_qsplit(int BH, int N) {
+  if constexpr (D != 64 || CAUSAL) {
+    return false;
+  } else {
+    const int slots = dkdv64_slots();
+    if (slots <= 0) return false;
+    const int64_t wgs = (int64_t)BH * ((N + DkdvCfg<64>::BKV - 1) / DkdvCfg<64>::BKV);
+    const int64_t full = wgs / slots, rest = wgs % slots;
+    return full < 4 && rest > 0 && 2 * rest <= slots;
+  }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const float* lse, const void* dout,
                          const float* delta, void* dk, void* dv, int BH, int N, float scale, const BlockMask& m,
@@ -682,6 +775,16 @@ hipError_t launch_dkdv_t(const void* q, const void* k, const void* v, const floa
   else if (dr.on)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false, true>), ATTN_DKDV_ARGS, (const uint8_t*)nullptr, 0, 0,
                        dr.t, dr.seed_lo, dr.seed_hi, dr.inv_keep, sc.mode);
+  else if (dkdv_qsplit<D, CAUSAL>(BH, N)) {
+    if constexpr (D == 64 && !CAUSAL) {
+      using CQ = DkdvCfg<D, true>;
+      const int n_kq = (N + CQ::BKV - 1) / CQ::BKV;
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false, false, false, true>), dim3(BH * n_kq), dim3(256), 0,
+                         stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta,
+                         (bf16*)dk, (bf16*)dv, N, n_kq, BH * n_kq, sc.c, scale, (const uint8_t*)nullptr, 0, 0, 0u, 0u,
+                         0u, 1.f, sc.mode);
+    }
+  }
   else if (CAUSAL && BH % 8 == 0 && n_kt % 2 == 0 && n_kt <= kDkdvPairMaxTiles)
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, false, false, true>), dim3(total / 2), dim3(256), 0, stream,
                        (const bf16*)q, (const bf16*)k, (const bf16*)v, lse, (const bf16*)dout, delta, (bf16*)dk,

@@ -30,9 +30,12 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it and returns; it never synchronises.  The caller owns
  *     all buffers and keeps them alive until the stream has passed the work.
- *   - The library allocates no device memory and keeps no global state, except
+ *   - The library allocates no device memory and keeps no device state, except
  *     the static scratch array of attn_bwd_noalloc (see there); calls of the
- *     other entry points on different streams may run concurrently.
+ *     other entry points on different streams may run concurrently.  On the
+ *     host it caches, per device, two figures it queries once (resident
+ *     workgroups of one backward kernel, and the address of the scratch array),
+ *     under a lock.
  *   - Validation happens before anything is enqueued.  On any error nothing is
  *     launched and no output is written.  ATTN_OK means "enqueued"; a device
  *     fault shows up at the caller's next synchronisation.

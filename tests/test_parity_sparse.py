@@ -101,10 +101,21 @@ def test_small_block_sparse_matches_oracle(attn, B, H, N, d, causal, shared):
             assert torch.all(torch.isneginf(got["lse"][b, h][dead]))
 
 
+def _within_one_bf16_ulp(a, b):
+    """|a - b| at most one bf16 spacing at max(|a|, |b|) (8 significant bits)."""
+    a32, b32 = a.float(), b.float()
+    return bool(torch.all((a32 - b32).abs() <= torch.maximum(a32.abs(), b32.abs()) * 2.0**-7 + 1e-6))
+
+
 @pytest.mark.parametrize("N,d,causal", [(384, 64, False), (300, 128, True), (1000, 128, True)])
 def test_all_blocks_on_equals_dense(attn, N, d, causal):
     """Every block on: the block-sparse kernels visit the same tiles in the same
-    order as the dense ones, so the results are bit-identical."""
+    order as the dense ones, so the results are bit-identical.  One exception:
+    the dense dK, dV kernel at d = 64, not causal, may split each key group's
+    queries over two waves and add the two partial sums at the end (when the
+    launch would otherwise end with a mostly empty round); that changes the fp32
+    summation order, so there dK and dV agree within one bf16 unit in the last
+    place."""
     _say(f"all-on mask N={N} d={d} causal={causal}")
     inp = W.draw(1, 2, N, d, "bf16", seed=3100 + N)
     q, k, v, do = (inp[x].cuda() for x in ("q", "k", "v", "do"))
@@ -116,8 +127,14 @@ def test_all_blocks_on_equals_dense(attn, N, d, causal):
     g_s = attn.bwd_block_sparse(q, k, v, o_s, l_s, do, ones, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o_d, o_s) and torch.equal(l_d, l_s)
-    for a, b in zip(g_d, g_s):
-        assert torch.equal(a, b)
+    dq_d, dk_d, dv_d = g_d
+    dq_s, dk_s, dv_s = g_s
+    assert torch.equal(dq_d, dq_s)
+    for a, b in ((dk_d, dk_s), (dv_d, dv_s)):
+        if d == 64 and not causal:
+            assert _within_one_bf16_ulp(a, b)
+        else:
+            assert torch.equal(a, b)
 
 
 def test_all_blocks_off(attn):
