@@ -572,6 +572,130 @@ fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K, const f
   }
 }
 
+
+// fp32 forward for small problems: the same arithmetic, split further.  A
+// workgroup owns 16 query rows; four threads share a row as above.  The
+// kF32Waves waves split the keys: wave w takes the 16-key tiles w, w + 8,
+// w + 16, ... of the row block's range, each staged in an LDS region of its
+// own (its lanes write a tile and then read it, in program order, so the loop
+// has no barrier), with its own running max, sum and accumulator.  At the end
+// the partial results of each row are merged through LDS the way the online
+// update merges blocks.  Small problems are latency bound: the time is the
+// serial length of one wave's key loop, which the split of the keys cuts by
+// the number of waves, and 16 rows per workgroup spread one head of 128 rows
+// over eight workgroups instead of two.  On large problems the 64-row kernel
+// is faster: each of its K/V tiles serves four times the rows, in a quarter
+// of the LDS.
+constexpr int kF32Waves = 8;
+// The split kernel runs when the 64-row kernel would launch fewer workgroups
+// than this (two per CU of a 256-CU GPU).  Measured: one head of N = 128,
+// 34 -> 16 us; four heads of N = 2048, 0.50 -> 0.17 ms; and, past the limit,
+// 2.4x slower than the 64-row kernel at 16 heads of N = 4096, d = 128.
+constexpr int kF32SplitBelow = 512;
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(64 * kF32Waves)
+fwd_f32_split_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+                     float* __restrict__ O, float* __restrict__ L, int N, int n_qtiles, float c, uint32_t smode) {
+  constexpr int BC = 16;     // keys per tile
+  constexpr int RW = 16;     // query rows per workgroup
+  constexpr int DP = D / 4;  // columns per thread
+  constexpr int KW = kF32Waves;
+  constexpr int NT = 64 * KW;  // threads
+  // per wave: a K tile and a V tile; after the key loop, the merge area
+  __shared__ float sm[KW][2][BC][D];
+  static_assert((DP + 2) * NT <= KW * 2 * BC * D, "the merge area fits in the tile regions");
+  const int bh = blockIdx.x / n_qtiles;
+  const int qt = blockIdx.x % n_qtiles;
+  const size_t head = (size_t)bh * N * D;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int d0 = (lane & 3) * DP;
+  const int q = qt * RW + (lane >> 2);
+  const bool qv = q < N;
+
+  float qr[DP], acc[DP];
+#pragma unroll
+  for (int i = 0; i < DP; ++i) {
+    qr[i] = sign_f32(qv ? Q[head + (size_t)q * D + d0 + i] : 0.f, smode);
+    acc[i] = 0.f;
+  }
+  float m_run = -1e30f, l_run = 0.f;
+  const int kv_end = CAUSAL ? min(N, qt * RW + RW) : N;
+  const int n_tiles = (kv_end + BC - 1) / BC;
+  float (*Ks)[D] = sm[wave][0];
+  float (*Vs)[D] = sm[wave][1];
+  for (int t = wave; t < n_tiles; t += KW) {
+    const int kv0 = t * BC;
+    for (int idx = lane; idx < BC * D; idx += 64) {
+      const int row = idx / D, col = idx % D;
+      const int key = kv0 + row;
+      Ks[row][col] = key < N ? K[head + (size_t)key * D + col] : 0.f;
+      Vs[row][col] = key < N ? V[head + (size_t)key * D + col] : 0.f;
+    }
+    float s[BC];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < BC; ++j) {
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < DP; ++i) dot = fmaf(qr[i], Ks[j][d0 + i], dot);
+      dot += __shfl_xor(dot, 1);
+      dot += __shfl_xor(dot, 2);
+      const int key = kv0 + j;
+      const bool bad = key >= N || (CAUSAL && key > q);
+      s[j] = bad ? -INFINITY : dot;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m_run, mx * c);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int i = 0; i < DP; ++i) acc[i] *= alpha;
+#pragma unroll
+    for (int j = 0; j < BC; ++j) {
+      const float p = exp2f(fmaf(s[j], c, -m_new));
+      rs += p;
+#pragma unroll
+      for (int i = 0; i < DP; ++i) acc[i] = fmaf(p, Vs[j][d0 + i], acc[i]);
+    }
+    l_run = l_run * alpha + rs;
+  }
+
+  // merge: slot (i, thread) of the area holds accumulator column i, then m and l
+  __syncthreads();  // every wave is done with its tiles
+  float* mg = &sm[0][0][0][0];
+#pragma unroll
+  for (int i = 0; i < DP; ++i) mg[i * NT + threadIdx.x] = acc[i];
+  mg[DP * NT + threadIdx.x] = m_run;
+  mg[(DP + 1) * NT + threadIdx.x] = l_run;
+  __syncthreads();
+  if (wave == 0 && qv) {
+    // a wave that saw no allowed key has m = -1e30 and weight 0; wave 0 holds key 0
+    float mw[KW], mmax = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < KW; ++w) {
+      mw[w] = mg[DP * NT + w * 64 + lane];
+      mmax = fmaxf(mmax, mw[w]);
+    }
+    float wt[KW], lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < KW; ++w) {
+      wt[w] = exp2f(mw[w] - mmax);
+      lt = fmaf(mg[(DP + 1) * NT + w * 64 + lane], wt[w], lt);
+    }
+    const float inv = 1.0f / lt;
+#pragma unroll
+    for (int i = 0; i < DP; ++i) {
+      float o = 0.f;
+#pragma unroll
+      for (int w = 0; w < KW; ++w) o = fmaf(mg[i * NT + w * 64 + lane], wt[w], o);
+      O[head + (size_t)q * D + d0 + i] = o * inv;
+    }
+    if (d0 == 0) L[(size_t)bh * N + q] = (mmax + log2f(lt)) * kLn2;
+  }
+}
+
 // Longest causal sequence, in 128-row query tiles, that runs as pairs of tiles
 // per workgroup (measured: 2.6% faster at 64 tiles, 10% at 32; 1% slower at
 // 256, where each workgroup is long anyway and a second head's keys and
@@ -616,11 +740,16 @@ hipError_t launch_fwd_bf16_t(const void* q, const void* k, const void* v, void* 
 template <int D, bool CAUSAL>
 hipError_t launch_fwd_f32_t(const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                             int N, float scale, hipStream_t stream) {
-  const int n_qtiles = (N + 63) / 64;
   const ScoreScale sc = split_scale(scale);
-  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(BH * n_qtiles), dim3(256), 0, stream,
-                     (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, N, n_qtiles, sc.c,
-                     sc.mode);
+  const int n_qtiles = (N + 63) / 64;
+  if ((int64_t)BH * n_qtiles < kF32SplitBelow) {
+    const int n_rt = (N + 15) / 16;
+    hipLaunchKernelGGL((fwd_f32_split_kernel<D, CAUSAL>), dim3(BH * n_rt), dim3(64 * kF32Waves), 0, stream,
+                       (const float*)q, (const float*)k, (const float*)v, (float*)o, lse, N, n_rt, sc.c, sc.mode);
+  } else {
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(BH * n_qtiles), dim3(256), 0, stream, (const float*)q,
+                       (const float*)k, (const float*)v, (float*)o, lse, N, n_qtiles, sc.c, sc.mode);
+  }
   return hipGetLastError();
 }
 

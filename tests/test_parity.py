@@ -83,6 +83,19 @@ def test_fp32_forward(attn, N, d, causal):
     compare_heads(got, oracle_full(inp, scale, causal, False), f"f32 N={N}", fp32=True)
 
 
+@pytest.mark.parametrize("H,N,d,causal", [(16, 2048, 64, False), (16, 2048, 128, True)])
+def test_fp32_forward_many_heads(attn, H, N, d, causal):
+    """B*H*ceil(N/64) = 512 workgroups: the 64-row fp32 kernel (smaller problems
+    take the one that splits each row block's keys over eight waves)."""
+    w = W.WORKLOADS[0]
+    inp = W.draw(1, H, N, d, "f32", seed=w.seed + 5 * N + d, backward=False)
+    scale = 1 / math.sqrt(d)
+    _say(f"fp32 fwd H={H} N={N} d={d} causal={causal}")
+    got = run_gpu(attn, inp, scale, causal, False)
+    compare_heads(got, oracle_full(inp, scale, causal, False, heads=[(0, 0), (0, H - 1)]), f"f32 H={H} N={N}",
+                  fp32=True)
+
+
 def test_fp32_small_workload_full(attn):
     w = W.BY_NAME["fp32_small"]
     inp = W.draw_workload(w)
