@@ -10,8 +10,9 @@
 // Design (MI355X): decode reads every cached key and value once and does
 // ~2 FLOPs per byte, so it is bound by HBM bandwidth, not by the matrix
 // cores.  The work is split over the keys:
-//   * decode_partial_kernel: one workgroup per (batch*head, 512-key chunk).
-//     Four threads per key form the chunk's scores for every query (16-byte
+//   * decode_partial_kernel (one query) or decode_mma_kernel (two or more,
+//     both products on the matrix cores; see there): one workgroup per
+//     (batch*head, 512-key chunk).  In the first, four threads per key form the chunk's scores for every query (16-byte
 //     loads of K kept as bf16 pairs, v_dot2_f32_bf16 against q held in LDS as
 //     bf16 pairs, two DPP adds); one wave per query takes the chunk max and
 //     exp-sum; then 16 (d=128) or 32 (d=64) key lanes accumulate
@@ -38,8 +39,9 @@ constexpr int kDecChunk = 512;  // keys per workgroup
 constexpr int kDecTile = 64;    // keys per pass-1 tile (4 threads per key)
 constexpr int kDecMaxQ = 8;     // most queries per call
 
-// NQ: query capacity of the instantiation (1, 2, 4 or 8 >= nq); registers and
-// LDS scale with it, so a one-query call keeps more workgroups per CU in flight
+// NQ: query capacity of the instantiation (>= nq); registers and LDS scale
+// with it.  The launcher instantiates it for one query only (more go to
+// decode_mma_kernel), which keeps many workgroups per CU in flight
 template <int D, int NQ>
 __global__ void __launch_bounds__(256)
 decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -183,37 +185,214 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
   }
 }
 
+// v_mfma_f32_16x16x32_bf16 (wave64): lane l holds A[l % 16][8 * (l / 16) + e],
+// B[8 * (l / 16) + e][l % 16] (e = 0..7) and C[4 * (l / 16) + i][l % 16]
+// (i = 0..3).  As for the 32x32 product, only the pairing of the k slots of A
+// and B matters.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// The same partial results as decode_partial_kernel with both products on the
+// matrix cores, for calls with several queries: with eight of them the two
+// v_dot2 passes kept the vector ALUs about half busy and the loads waited on
+// them.  Each wave owns 128 keys of the chunk in both products, and both are
+// 16x16x32 products with the queries padded to 16 rows (zeros):
+//   * scores: S = Q K^T, A = Q from registers, B = K^T loaded straight from
+//     HBM (lane l holds key l % 16, dims 32 st + 8 (l / 16) + e, so one load
+//     covers 64 contiguous bytes of 16 keys); C register i of lanes 0-31
+//     holds query 4 (l / 16) + i of key l % 16.  The next 16 keys' loads are
+//     issued before the current products;
+//   * p V: O = P V.  B must hold 8 keys of one value column per lane, while V
+//     rows run along the dims, so each lane loads D / 16 dims of 8 keys (keys
+//     8 (l / 16) + e of the step, 8 or 16 contiguous bytes each) and regroups
+//     them with v_perm into one operand per dim: column l % 16 of product t
+//     is dim (D / 16) (l % 16) + t.  P comes from LDS as bf16, rounded as in
+//     the forward kernel; l sums the unrounded p.
+// The four waves' partial O meet in LDS in the space the scores used.
+template <int D>
+__global__ void __launch_bounds__(256)
+decode_mma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                  float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, int Nk, int nq, int S,
+                  float c, int causal) {
+  constexpr int KS = D / 32;                 // 32-dim steps of the score product
+  constexpr int KPW = kDecChunk / 4;         // keys per wave
+  constexpr int DPL = D / 16;                // value dims per lane (= products per p V step)
+  static_assert(4 * kDecMaxQ * D <= kDecMaxQ * kDecChunk, "partial O fits in the score space");
+  __shared__ __attribute__((aligned(16))) float sbuf[kDecMaxQ * kDecChunk];
+  __shared__ __attribute__((aligned(16))) bf16 p16[kDecMaxQ][kDecChunk];
+  float (*sc)[kDecChunk] = reinterpret_cast<float (*)[kDecChunk]>(sbuf);
+
+  const int bh = blockIdx.x / S;
+  const int s = blockIdx.x % S;
+  const int k0 = s * kDecChunk;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kw = KPW * wave;  // first key of this wave, relative to k0
+  const uint32_t head_bytes = (uint32_t)Nk * D * 2;
+  const rsrc_t rK = make_rsrc(K + (size_t)bh * Nk * D, head_bytes);
+  const rsrc_t rV = make_rsrc(V + (size_t)bh * Nk * D, head_bytes);
+
+  // ---- scores, in base-2 units; masked keys get -inf
+  {
+    const int n = lane & 15, g = lane >> 4;
+    u32x4 qa[KS];
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const u32x4* qrow = reinterpret_cast<const u32x4*>(Q + ((size_t)bh * nq + (n < nq ? n : 0)) * D);
+#pragma unroll
+    for (int st = 0; st < KS; ++st) qa[st] = n < nq ? qrow[4 * st + g] : zero;
+    constexpr int PF = 1;  // blocks of K loads issued ahead (more costs occupancy at d = 128)
+    u32x4 kv[PF + 1][KS];
+    auto kload = [&](int b, u32x4 (&dst)[KS]) {
+      const uint32_t row = (uint32_t)(k0 + kw + 16 * b + n) * (D * 2) + 16u * g;
+#pragma unroll
+      for (int st = 0; st < KS; ++st) dst[st] = bload16(rK, (int)(row + 64u * st), 0);
+    };
+#pragma unroll
+    for (int b = 0; b < PF; ++b) kload(b, kv[b]);
+#pragma unroll
+    for (int b = 0; b < KPW / 16; ++b) {
+      if (b + PF < KPW / 16) kload(b + PF, kv[(b + PF) % (PF + 1)]);
+      const int key = k0 + kw + 16 * b + n;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < KS; ++st)
+        acc = mfma16(__builtin_bit_cast(bf16x8, qa[st]), __builtin_bit_cast(bf16x8, kv[b % (PF + 1)][st]), acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int qi = 4 * g + i;
+        if (qi < nq) {
+          const bool ok = key < Nk && (!causal || key <= Nk - nq + qi);
+          sc[qi][kw + 16 * b + n] = ok ? acc[i] * c : -INFINITY;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- chunk max and exp-sum per query (one wave per query); P as bf16
+  for (int qi = wave; qi < nq; qi += 4) {
+    float m = -INFINITY;
+    for (int i = lane; i < kDecChunk; i += 64) m = fmaxf(m, sc[qi][i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float l = 0.f;
+    for (int i = lane; i < kDecChunk; i += 64) {
+      const float p = m == -INFINITY ? 0.f : fast_exp2(sc[qi][i] - m);
+      p16[qi][i] = to_bf16(p);
+      l += p;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+    if (lane == 0) {
+      ws_m[((size_t)bh * S + s) * nq + qi] = m;
+      ws_l[((size_t)bh * S + s) * nq + qi] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- unnormalised O_c = P V over the chunk (scores are dead: the partial
+  // results of the waves reuse their space)
+  {
+    const int n = lane & 15, g = lane >> 4;
+    f32x4 acc[DPL];
+#pragma unroll
+    for (int t = 0; t < DPL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+    for (int j = 0; j < KPW / 32; ++j) {
+      const int kb = kw + 32 * j + 8 * g;  // first of this lane's 8 keys, relative to k0
+      const uint32_t row = (uint32_t)(k0 + kb) * (D * 2) + (uint32_t)(DPL * 2) * n;
+      uint32_t w[8][DPL / 2];  // w[e][x]: dims 2x, 2x + 1 (of this lane's DPL) of key kb + e
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (DPL == 8) {
+          const u32x4 x = bload16(rV, (int)(row + (uint32_t)(D * 2) * e), 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[e][i] = x[i];
+        } else {
+          const u32x2 x = bload8(rV, (int)(row + (uint32_t)(D * 2) * e), 0);
+          w[e][0] = x[0];
+          w[e][1] = x[1];
+        }
+      }
+      u32x4 a = {0u, 0u, 0u, 0u};
+      if (n < nq) a = *reinterpret_cast<const u32x4*>(&p16[n][kb]);
+#pragma unroll
+      for (int t = 0; t < DPL; ++t) {
+        const uint32_t sel = (t & 1) ? 0x07060302u : 0x05040100u;  // high or low bf16 of each word
+        u32x4 bt;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) bt[x] = __builtin_amdgcn_perm(w[2 * x + 1][t / 2], w[2 * x][t / 2], sel);
+        acc[t] = mfma16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bt), acc[t]);
+      }
+    }
+    float (*red)[kDecMaxQ][D] = reinterpret_cast<float (*)[kDecMaxQ][D]>(sbuf);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int qi = 4 * g + i;
+      if (qi < nq) {
+#pragma unroll
+        for (int t = 0; t < DPL; ++t) red[wave][qi][DPL * n + t] = acc[t][i];
+      }
+    }
+  }
+  __syncthreads();
+  {
+    float (*red)[kDecMaxQ][D] = reinterpret_cast<float (*)[kDecMaxQ][D]>(sbuf);
+    for (int idx = tid; idx < nq * D; idx += 256) {
+      const int qi = idx / D, dd = idx % D;
+      const float o = red[0][qi][dd] + red[1][qi][dd] + red[2][qi][dd] + red[3][qi][dd];
+      ws_o[(((size_t)bh * S + s) * nq + qi) * D + dd] = o;
+    }
+  }
+}
+
 template <int D>
 __global__ void __launch_bounds__(D)
 decode_merge_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws_l, const float* __restrict__ ws_o,
                     bf16* __restrict__ O, float* __restrict__ L, int nq, int S) {
-  constexpr int NW = D / 64;
-  __shared__ float wmax[NW];
+  constexpr int NB = 32;  // chunks whose loads are in flight together
   const int bh = blockIdx.x / nq, qi = blockIdx.x % nq;
   const int dd = threadIdx.x;
+  const int lane = dd & 63;
   const size_t base = (size_t)bh * S * nq + qi;  // partial s of this query sits at base + s * nq
-  // the reference max over the chunks: the threads share the chunks, then
-  // the waves combine their maxima through LDS (all loads independent)
+  // buffer resources over this query's partials: chunk s is a scalar offset
+  // of s * nq words (times D for O), and chunks past S read as zero
+  const uint32_t span = (uint32_t)S * nq * 4;
+  const rsrc_t rm = make_rsrc(ws_m + base, span);
+  const rsrc_t rl = make_rsrc(ws_l + base, span);
+  const rsrc_t ro = make_rsrc(ws_o + base * D, span * D);
+  float ob[NB], mb[NB], lb[NB];
+  const int step = nq * 4;  // bytes from one chunk's m (or l) to the next
+  auto fetch = [&](int s0) {
+    int so = s0 * step;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      ob[i] = __uint_as_float(bload4(ro, 4 * dd, so * D));
+      mb[i] = __uint_as_float(bload4(rm, 0, so));
+      lb[i] = __uint_as_float(bload4(rl, 0, so));
+      so += step;
+    }
+  };
+  // the first chunks are requested before the max is known; each wave
+  // reduces the max over all chunks on its own, so both round trips overlap
+  fetch(0);
   float m = -INFINITY;
-  for (int s = dd; s < S; s += D) m = fmaxf(m, ws_m[base + (size_t)s * nq]);
+  for (int s = lane; s < S; s += 64) m = fmaxf(m, __uint_as_float(bload4(rm, 4 * s * nq, 0)));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((dd & 63) == 0) wmax[dd >> 6] = m;
-  __syncthreads();
-  m = wmax[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) m = fmaxf(m, wmax[w]);
   float l = 0.f, o = 0.f;
   if (m != -INFINITY) {
-    // each thread sums its d column; the chunks' loads do not depend on each
-    // other, so unrolling keeps several in flight
-#pragma unroll 8
-    for (int s = 0; s < S; ++s) {
-      const size_t p = base + (size_t)s * nq;
-      const float ms = ws_m[p];
-      const float a = ms == -INFINITY ? 0.f : fast_exp2(ms - m);
-      l = fmaf(a, ws_l[p], l);
-      o = fmaf(a, ws_o[p * D + dd], o);
+    // chunks in order, so the sums round the same way for any batch size
+    for (int s0 = 0; s0 < S; s0 += NB) {
+      if (s0 > 0) fetch(s0);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const float a = (s0 + i >= S || mb[i] == -INFINITY) ? 0.f : fast_exp2(mb[i] - m);
+        l = fmaf(a, lb[i], l);
+        o = fmaf(a, ob[i], o);
+      }
     }
   }
   const bool empty = l == 0.f;
@@ -240,10 +419,11 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, f
       hipLaunchKernelGGL((decode_partial_kernel<D, decltype(nqc)::value>), dim3(BH * S), dim3(256), 0, stream,
                          (const bf16*)q, (const bf16*)k, (const bf16*)v, ws_m, ws_l, ws_o, Nk, Nq, S, c, (int)causal);
     };
+    // the matrix-core kernel measured faster from two queries up
     if (Nq == 1) go(std::integral_constant<int, 1>{});
-    else if (Nq <= 2) go(std::integral_constant<int, 2>{});
-    else if (Nq <= 4) go(std::integral_constant<int, 4>{});
-    else go(std::integral_constant<int, kDecMaxQ>{});
+    else
+      hipLaunchKernelGGL((decode_mma_kernel<D>), dim3(BH * S), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
+                         (const bf16*)v, ws_m, ws_l, ws_o, Nk, Nq, S, c, (int)causal);
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(BH * Nq), dim3(D), 0, stream, ws_m, ws_l, ws_o, (bf16*)o, lse,
                        Nq, S);
   };
