@@ -394,6 +394,20 @@ def bench_probe(args):
     ref = np.exp2(xs)
     ulp = np.spacing(ref.astype(np.float32)).astype(np.float64)
     out["v_exp_f32_max_ulp_on_-39.5_0.5"] = round(float(np.max(np.abs(ys - ref) / ulp)), 3)
+    # HBM read rate: a 4 GiB buffer (twice the L2s and the last-level cache many
+    # times over) read once per launch, over grid sizes and loads in flight
+    src = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    src.view(torch.int32).fill_(0x01020304)
+    rd = {}
+    for per_cu in (4, 8, 16, 32):
+        wgs = cus * per_cu
+        sink = torch.empty(wgs * 256, dtype=torch.int32, device=dev)
+        for unroll in (1, 2, 4, 8):
+            ms = timed(lambda: lib.attn_probe_read_rate(P(src), src.numel(), unroll, wgs, P(sink), st), reps=5)
+            rd[f"{per_cu} workgroups/CU, {unroll} loads in flight"] = round(src.numel() / (ms * 1e-3) / 1e9, 1)
+    out["hbm_read_gb_per_s"] = rd
+    out["hbm_read_best_gb_per_s"] = max(rd.values())
+    del src
     out["host"] = host_facts()
     print(json.dumps(out), flush=True)
     return 0

@@ -50,6 +50,7 @@ _SIGNATURES = {
     "attn_probe_wave_simd": (_I, [_I, _P, _P]),
     "attn_probe_atomic": (_I, [_P, _S, _I, _P]),
     "attn_probe_exp2": (_I, [_P, _P, _S, _P]),
+    "attn_probe_read_rate": (_I, [_P, _S, _I, _I, _P, _P]),
 }
 
 

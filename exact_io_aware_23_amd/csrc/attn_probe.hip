@@ -15,6 +15,9 @@
 //   attn_probe_atomic     fp32 global atomic adds, or the same update as a
 //                         plain load, add and store, over a region.
 //   attn_probe_exp2       y = v_exp_f32(x) elementwise, for an accuracy sweep.
+//   attn_probe_read_rate  a read-only stream over a device buffer (16-byte
+//                         loads, a chosen number in flight per thread): the
+//                         HBM read rate a bandwidth-bound kernel can reach.
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
@@ -145,6 +148,29 @@ __global__ void __launch_bounds__(256) exp2_kernel(const float* __restrict__ x, 
   if (i < n) y[i] = __builtin_amdgcn_exp2f(x[i]);
 }
 
+// Thread t of the grid reads 16-byte words t, t + T, t + 2T, ... (T threads in
+// all), U of them issued before any is used; the words are folded into one
+// value per thread so the loads stay live.
+template <int U>
+__global__ void __launch_bounds__(256) read_kernel(const u32x4* __restrict__ src, size_t n16,
+                                                   unsigned* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  unsigned acc = 0;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const u32x4 v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  sink[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 }  // namespace
 }  // namespace attn_probe
 
@@ -184,6 +210,21 @@ int attn_probe_atomic(float* target, size_t n, int atomic, hipStream_t stream) {
 int attn_probe_exp2(const float* x, float* y, size_t n, hipStream_t stream) {
   if (!x || !y || n == 0 || (n + 255) / 256 > (size_t)(1u << 31)) return 1;
   hipLaunchKernelGGL(exp2_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, x, y, n);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int attn_probe_read_rate(const void* src, size_t bytes, int unroll, int workgroups, unsigned* sink,
+                         hipStream_t stream) {
+  if (!src || !sink || bytes == 0 || bytes % 16 != 0 || workgroups <= 0 || workgroups > (1 << 20)) return 1;
+  const u32x4* p = static_cast<const u32x4*>(src);
+  const size_t n16 = bytes / 16;
+  switch (unroll) {
+    case 1: hipLaunchKernelGGL(read_kernel<1>, dim3(workgroups), dim3(256), 0, stream, p, n16, sink); break;
+    case 2: hipLaunchKernelGGL(read_kernel<2>, dim3(workgroups), dim3(256), 0, stream, p, n16, sink); break;
+    case 4: hipLaunchKernelGGL(read_kernel<4>, dim3(workgroups), dim3(256), 0, stream, p, n16, sink); break;
+    case 8: hipLaunchKernelGGL(read_kernel<8>, dim3(workgroups), dim3(256), 0, stream, p, n16, sink); break;
+    default: return 1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

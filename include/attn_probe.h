@@ -1,6 +1,6 @@
 /* Hardware probes for MI355X (gfx950): measurement aids behind the rates the
  * design quotes (LDS read throughput, instruction issue rates, wave placement,
- * global atomic throughput, v_exp_f32 accuracy).  Not part of the attention
+ * global atomic throughput, v_exp_f32 accuracy, HBM read rate).  Not part of the attention
  * ABI in attn.h; libattn.so exports them beside it.
  *
  * Common rules: every pointer is a device pointer owned by the caller, sized as
@@ -47,6 +47,13 @@ int attn_probe_atomic(float* target, size_t n, int atomic, hipStream_t stream);
 
 /* y[i] = v_exp_f32(x[i]) (the exp2 every kernel's softmax uses), i < n. */
 int attn_probe_exp2(const float* x, float* y, size_t n, hipStream_t stream);
+
+/* HBM read rate: `workgroups` workgroups of 256 threads read the `bytes` bytes
+ * at src (a multiple of 16, 16-byte aligned) once, as 16-byte loads, each
+ * thread keeping `unroll` (1, 2, 4 or 8) loads in flight; sink[workgroups *
+ * 256] receives a value per thread that keeps the loads alive. */
+int attn_probe_read_rate(const void* src, size_t bytes, int unroll, int workgroups, unsigned* sink,
+                         hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -41,7 +41,8 @@ def test_header_declares_the_expected_entry_points():
 
 def test_probe_header_declares_the_probes():
     assert declared_functions(PROBE_HEADER) == sorted([
-        "attn_probe_lds_rate", "attn_probe_issue", "attn_probe_wave_simd", "attn_probe_atomic", "attn_probe_exp2"])
+        "attn_probe_lds_rate", "attn_probe_issue", "attn_probe_wave_simd", "attn_probe_atomic", "attn_probe_exp2",
+        "attn_probe_read_rate"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -65,6 +66,10 @@ def test_probe_validation(lib):
     assert lib.attn_probe_atomic(FAKE, 100, 1, None) == 1  # not a multiple of 16384
     assert lib.attn_probe_atomic(None, 16384, 1, None) == 1
     assert lib.attn_probe_exp2(FAKE, FAKE, 0, None) == 1
+    assert lib.attn_probe_read_rate(FAKE, 100, 4, 8, FAKE, None) == 1  # not a multiple of 16
+    assert lib.attn_probe_read_rate(FAKE, 1 << 20, 3, 8, FAKE, None) == 1  # unroll not 1, 2, 4 or 8
+    assert lib.attn_probe_read_rate(FAKE, 1 << 20, 4, 0, FAKE, None) == 1
+    assert lib.attn_probe_read_rate(None, 1 << 20, 4, 8, FAKE, None) == 1
 
 
 def test_abi_version_matches_header(lib):
