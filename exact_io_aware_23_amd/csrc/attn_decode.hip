@@ -12,10 +12,11 @@
 // cores.  The work is split over the keys:
 //   * decode_partial_kernel (one query) or decode_mma_kernel (two or more,
 //     both products on the matrix cores; see there): one workgroup per
-//     (batch*head, 512-key chunk).  In the first, four threads per key form the chunk's scores for every query (16-byte
-//     loads of K kept as bf16 pairs, v_dot2_f32_bf16 against q held in LDS as
-//     bf16 pairs, two DPP adds); one wave per query takes the chunk max and
-//     exp-sum; then 16 (d=128) or 32 (d=64) key lanes accumulate
+//     (batch*head, 512-key chunk).  In the first, four threads per key form
+//     the chunk's scores for every query (16-byte loads of K kept as bf16
+//     pairs, v_dot2_f32_bf16 against q held in LDS as bf16 pairs, two DPP
+//     adds); one wave per query takes the chunk max and exp-sum; then 16
+//     (d=128) or 32 (d=64) key lanes accumulate
 //     sum_j p_j V_j two keys at a time: the two V rows are interleaved into
 //     bf16 pairs, p of both keys is rounded to one bf16 pair (as the forward
 //     rounds P before its P V product; l sums the unrounded p), and one
@@ -209,9 +210,10 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 //     them with v_perm into one operand per dim: column l % 16 of product t
 //     is dim (D / 16) (l % 16) + t.  P comes from LDS as bf16, rounded as in
 //     the forward kernel; l sums the unrounded p.
-// The four waves' partial O meet in LDS in the space the scores used.
-// (capped at 80 registers: six workgroups per CU, as the LDS allows; 1-2%
-// faster than the uncapped 94 at d = 128, no spills)
+// The four waves' partial O meet in LDS in the space the scores used.  The
+// launch bounds cap it at 80 registers, so six workgroups share a CU, as many
+// as its 24 KB of LDS allow (1-2% faster than the uncapped 94 at d = 128; no
+// spills).
 template <int D>
 __global__ void __launch_bounds__(256, 6)
 decode_mma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
