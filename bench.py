@@ -418,7 +418,7 @@ def kernel_source_hash(kernel: str) -> str:
     import hashlib
 
     src = {"fwd": "attn_fwd.hip", "preprocess": "attn_bwd.hip", "dq": "attn_bwd.hip", "dkdv": "attn_bwd.hip",
-           "fwd_fp8": "attn_fwd_fp8.hip"}[kernel]
+           "fwd_fp8": "attn_fwd_fp8.hip", "decode_partial": "attn_decode.hip", "decode_merge": "attn_decode.hip"}[kernel]
     h = hashlib.sha256()
     for f in (src, "attn_common.h"):
         with open(os.path.join(ROOT, "exact_io_aware_23_amd", "csrc", f), "rb") as fh:
@@ -491,6 +491,10 @@ def bench_decode(args):
     # algorithmic bytes: K and V once, q in, O and L out
     bytes_ = 2.0 * B * H * Nk * d * 2 + 2.0 * B * H * Nq * d * 2 + 4.0 * B * H * Nq
     gbs = bytes_ / (t_gpu * 1e-3) / 1e9
+    # HBM bytes of one call (partial + merge kernel), from the committed counter summary of this shape
+    wl = f"decode_b{B}_h{H}_nq{Nq}_nk{Nk}_d{d}"
+    parts = [measured_traffic(kern, wl) for kern in ("decode_partial", "decode_merge")]
+    traffic = None if None in parts else sum(parts)
     out = {
         "metric": "decode attention GB/s against a KV cache (HBM roofline)",
         "value": round(gbs, 1),
@@ -508,8 +512,8 @@ def bench_decode(args):
         "gpu_ms_per_call": round(t_gpu, 4),
         "tflops": round(4.0 * d * Nq * Nk * B * H / (t_gpu * 1e-3) / 1e12, 3),
         "roofline": {"kernel": "decode (partial + merge)", "bound": "hbm", "achieved": round(gbs, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "avg_launch_ms": round(t_gpu, 4)},
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes": int(bytes_), "avg_launch_ms": round(t_gpu, 4)},
     }
     if not args.no_cpu_baseline:
         from oracle import decode as dec

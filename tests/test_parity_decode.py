@@ -40,7 +40,7 @@ def draw(B, H, Nq, Nk, d, seed):
     return q, cache["k"], cache["v"]
 
 
-@pytest.mark.parametrize("Nq,Nk", [(1, 1), (1, 100), (2, 700), (4, 512), (8, 513), (3, 1500), (1, 2049), (6, 2500), (7, 33)])
+@pytest.mark.parametrize("Nq,Nk", [(1, 1), (1, 100), (2, 700), (4, 512), (8, 513), (3, 1500), (1, 2049), (6, 2500), (7, 33), (8, 8)])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_decode_matches_oracle(attn, Nq, Nk, d, causal):
