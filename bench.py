@@ -24,6 +24,12 @@ the bf16 forward on the same shape beside it, priced against the fp8 peak.
 --decode-nk keys (B=4, H=32, d=128 unless --batch/--heads say otherwise),
 priced against HBM bandwidth (it reads each cached key and value once).
 
+--warmup W untimed steps come first.  For the first tens of milliseconds after
+the GPU leaves idle its clock is still ramping and the kernels run 10-20%
+slower, so a workload whose step takes under a millisecond wants W large enough
+for ~0.15 s of steps (e.g. 500 at N=2048, 2000 for bf16_n256_d64_short); at
+N >= 8192 the default 3 measures the same as 60.
+
 Reported:
   value         whole-step attention TFLOP/s, (F_fwd + F_bwd) / t_step, with the
                 algorithmic FLOP counts 4*B*H*N^2*d (halved when causal) and
@@ -62,7 +68,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=3,
+                    help="untimed steps first; sub-millisecond steps want ~0.15 s of them (the GPU clock ramps up)")
     ap.add_argument("--workload", default="bf16_n8192_d128_causal")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's B")
     ap.add_argument("--heads", type=int, default=None, help="override the workload's H (e.g. one GPU's share of heads)")
