@@ -280,7 +280,7 @@ attn_status_t attn_bwd_dropout(const void* q, const void* k, const void* v, cons
 size_t attn_decode_workspace_bytes(int B, int H, int Nq, int Nk, int d) {
   if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 0;
   if (Nq > attn::decode_max_queries() || Nk > (1 << 23) || (int64_t)B * H * Nk >= ((int64_t)1 << 31)) return 0;
-  const size_t parts = (size_t)B * H * attn::decode_chunks(Nk) * Nq;
+  const size_t parts = (size_t)B * H * attn::decode_chunks(B * H, Nk) * Nq;
   const size_t bytes = parts * (2 + (size_t)d) * sizeof(float);
   return (bytes + 255) & ~(size_t)255;
 }

@@ -28,6 +28,7 @@
 //     l = sum 2^(m_c - m) l_c, O = sum 2^(m_c - m) O_c / l.
 // Scores are kept in base-2 units (scale * log2 e folded in), as in the
 // forward kernel.
+#include <cstdint>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -36,14 +37,16 @@
 namespace attn {
 namespace {
 
-constexpr int kDecChunk = 512;  // keys per workgroup
+constexpr int kDecChunk = 512;  // keys per workgroup, most (a call with few heads and keys takes 256 or 128)
+constexpr int kDecMinChunk = 128;
+constexpr int kDecTargetWgs = 1024;  // workgroups a call should have to fill the GPU (four per CU)
 constexpr int kDecTile = 64;    // keys per pass-1 tile (4 threads per key)
 constexpr int kDecMaxQ = 8;     // most queries per call
 
 // NQ: query capacity of the instantiation (>= nq); registers and LDS scale
 // with it.  The launcher instantiates it for one query only (more go to
 // decode_mma_kernel), which keeps many workgroups per CU in flight
-template <int D, int NQ>
+template <int D, int NQ, int CH>
 __global__ void __launch_bounds__(256)
 decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                       float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, int Nk, int nq,
@@ -53,12 +56,12 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
   constexpr int KL = 256 / G8;       // key lanes in pass 2
   static_assert(NQ >= 1 && NQ <= kDecMaxQ, "query capacity");
   __shared__ __attribute__((aligned(16))) uint32_t qs2[NQ][D / 2];  // q as packed bf16 pairs
-  __shared__ float sc[NQ][kDecChunk];
+  __shared__ float sc[NQ][CH];
   __shared__ __attribute__((aligned(16))) float red[4][NQ][D];
 
   const int bh = blockIdx.x / S;
   const int s = blockIdx.x % S;
-  const int k0 = s * kDecChunk;
+  const int k0 = s * CH;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -76,7 +79,7 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
   {
     const int kl = tid >> 2, part = tid & 3;
 #pragma unroll 2
-    for (int kt = 0; kt < kDecChunk; kt += kDecTile) {
+    for (int kt = 0; kt < CH; kt += kDecTile) {
       const int key = k0 + kt + kl;
       // K stays packed: v_dot2_f32_bf16 takes two bf16 products per
       // instruction (each exact in fp32) and q comes from LDS as bf16 pairs
@@ -111,11 +114,11 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
   // ---- chunk max and exp-sum per query (one wave per query); p in place
   for (int qi = wave; qi < nq; qi += 4) {
     float m = -INFINITY;
-    for (int i = lane; i < kDecChunk; i += 64) m = fmaxf(m, sc[qi][i]);
+    for (int i = lane; i < CH; i += 64) m = fmaxf(m, sc[qi][i]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
     float l = 0.f;
-    for (int i = lane; i < kDecChunk; i += 64) {
+    for (int i = lane; i < CH; i += 64) {
       const float p = m == -INFINITY ? 0.f : fast_exp2(sc[qi][i] - m);
       sc[qi][i] = p;
       l += p;
@@ -140,7 +143,7 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
   // (one v_perm per pair) and p of both keys is rounded to one bf16 pair, so
   // each v_dot2_f32_bf16 adds two keys' products to a column
 #pragma unroll 2
-  for (int kj = kl2; kj < kDecChunk; kj += 2 * KL) {
+  for (int kj = kl2; kj < CH; kj += 2 * KL) {
     const u32x4 va = bload16(rV, ((k0 + kj) * D + 8 * g8) * 2, 0);
     const u32x4 vb = bload16(rV, ((k0 + kj + KL) * D + 8 * g8) * 2, 0);
     uint32_t pr[8];
@@ -214,22 +217,23 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 // launch bounds cap it at 80 registers, so six workgroups share a CU, as many
 // as its 24 KB of LDS allow (1-2% faster than the uncapped 94 at d = 128; no
 // spills).
-template <int D>
+template <int D, int CH>
 __global__ void __launch_bounds__(256, 6)
 decode_mma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                   float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, int Nk, int nq, int S,
                   float c, int causal) {
   constexpr int KS = D / 32;                 // 32-dim steps of the score product
-  constexpr int KPW = kDecChunk / 4;         // keys per wave
+  constexpr int KPW = CH / 4;         // keys per wave
   constexpr int DPL = D / 16;                // value dims per lane (= products per p V step)
-  static_assert(4 * kDecMaxQ * D <= kDecMaxQ * kDecChunk, "partial O fits in the score space");
-  __shared__ __attribute__((aligned(16))) float sbuf[kDecMaxQ * kDecChunk];
-  __shared__ __attribute__((aligned(16))) bf16 p16[kDecMaxQ][kDecChunk];
-  float (*sc)[kDecChunk] = reinterpret_cast<float (*)[kDecChunk]>(sbuf);
+  // the scores of the chunk, later the four waves' partial O
+  constexpr int SBUF = kDecMaxQ * CH > 4 * kDecMaxQ * D ? kDecMaxQ * CH : 4 * kDecMaxQ * D;
+  __shared__ __attribute__((aligned(16))) float sbuf[SBUF];
+  __shared__ __attribute__((aligned(16))) bf16 p16[kDecMaxQ][CH];
+  float (*sc)[CH] = reinterpret_cast<float (*)[CH]>(sbuf);
 
   const int bh = blockIdx.x / S;
   const int s = blockIdx.x % S;
-  const int k0 = s * kDecChunk;
+  const int k0 = s * CH;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -278,11 +282,11 @@ decode_mma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const 
   // ---- chunk max and exp-sum per query (one wave per query); P as bf16
   for (int qi = wave; qi < nq; qi += 4) {
     float m = -INFINITY;
-    for (int i = lane; i < kDecChunk; i += 64) m = fmaxf(m, sc[qi][i]);
+    for (int i = lane; i < CH; i += 64) m = fmaxf(m, sc[qi][i]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
     float l = 0.f;
-    for (int i = lane; i < kDecChunk; i += 64) {
+    for (int i = lane; i < CH; i += 64) {
       const float p = m == -INFINITY ? 0.f : fast_exp2(sc[qi][i] - m);
       p16[qi][i] = to_bf16(p);
       l += p;
@@ -303,8 +307,7 @@ decode_mma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const 
     f32x4 acc[DPL];
 #pragma unroll
     for (int t = 0; t < DPL; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-    for (int j = 0; j < KPW / 32; ++j) {
+    auto pv_step = [&](int j) {
       const int kb = kw + 32 * j + 8 * g;  // first of this lane's 8 keys, relative to k0
       const uint32_t row = (uint32_t)(k0 + kb) * (D * 2) + (uint32_t)(DPL * 2) * n;
       uint32_t w[8][DPL / 2];  // w[e][x]: dims 2x, 2x + 1 (of this lane's DPL) of key kb + e
@@ -330,6 +333,15 @@ decode_mma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const 
         for (int x = 0; x < 4; ++x) bt[x] = __builtin_amdgcn_perm(w[2 * x + 1][t / 2], w[2 * x][t / 2], sel);
         acc[t] = mfma16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, bt), acc[t]);
       }
+    };
+    // two steps a loop iteration (loads of the next step in flight); with
+    // only two steps in all that would hold both steps' loads at once
+    if constexpr (KPW / 32 > 2) {
+#pragma unroll 2
+      for (int j = 0; j < KPW / 32; ++j) pv_step(j);
+    } else {
+#pragma unroll 1
+      for (int j = 0; j < KPW / 32; ++j) pv_step(j);
     }
     float (*red)[kDecMaxQ][D] = reinterpret_cast<float (*)[kDecMaxQ][D]>(sbuf);
 #pragma unroll
@@ -406,33 +418,50 @@ decode_merge_kernel(const float* __restrict__ ws_m, const float* __restrict__ ws
 
 }  // namespace
 
-int decode_chunks(int Nk) { return (Nk + kDecChunk - 1) / kDecChunk; }
+// Keys per chunk: the largest of 512, 256 and 128 that still gives the call
+// kDecTargetWgs workgroups.  With 512 a call with few heads and a short cache
+// (one batch of 8 heads and 8192 keys: 128 workgroups) would leave most of
+// the 256 CUs idle.
+int decode_chunk_keys(int BH, int Nk) {
+  for (int ch = kDecChunk; ch > kDecMinChunk; ch /= 2)
+    if ((int64_t)BH * ((Nk + ch - 1) / ch) >= kDecTargetWgs) return ch;
+  return kDecMinChunk;
+}
+int decode_chunks(int BH, int Nk) {
+  const int ch = decode_chunk_keys(BH, Nk);
+  return (Nk + ch - 1) / ch;
+}
 int decode_max_queries() { return kDecMaxQ; }
 
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, float* ws, int BH,
                          int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream) {
-  const int S = decode_chunks(Nk);
+  const int ch = decode_chunk_keys(BH, Nk);
+  const int S = (Nk + ch - 1) / ch;
   const size_t parts = (size_t)BH * S * Nq;
   float* ws_m = ws;
   float* ws_l = ws + parts;
   float* ws_o = ws + 2 * parts;
   const float c = scale * kLog2e;
-  auto partial = [&](auto dq) {
+  auto partial = [&](auto dq, auto chc) {
     constexpr int D = decltype(dq)::value;
-    auto go = [&](auto nqc) {
-      hipLaunchKernelGGL((decode_partial_kernel<D, decltype(nqc)::value>), dim3(BH * S), dim3(256), 0, stream,
-                         (const bf16*)q, (const bf16*)k, (const bf16*)v, ws_m, ws_l, ws_o, Nk, Nq, S, c, (int)causal);
-    };
+    constexpr int CH = decltype(chc)::value;
     // the matrix-core kernel measured faster from two queries up
-    if (Nq == 1) go(std::integral_constant<int, 1>{});
+    if (Nq == 1)
+      hipLaunchKernelGGL((decode_partial_kernel<D, 1, CH>), dim3(BH * S), dim3(256), 0, stream, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, ws_m, ws_l, ws_o, Nk, Nq, S, c, (int)causal);
     else
-      hipLaunchKernelGGL((decode_mma_kernel<D>), dim3(BH * S), dim3(256), 0, stream, (const bf16*)q, (const bf16*)k,
-                         (const bf16*)v, ws_m, ws_l, ws_o, Nk, Nq, S, c, (int)causal);
+      hipLaunchKernelGGL((decode_mma_kernel<D, CH>), dim3(BH * S), dim3(256), 0, stream, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, ws_m, ws_l, ws_o, Nk, Nq, S, c, (int)causal);
     hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(BH * Nq), dim3(D), 0, stream, ws_m, ws_l, ws_o, (bf16*)o, lse,
                        Nq, S);
   };
-  if (d == 64) partial(std::integral_constant<int, 64>{});
-  else partial(std::integral_constant<int, 128>{});
+  auto by_chunk = [&](auto dq) {
+    if (ch == 512) partial(dq, std::integral_constant<int, 512>{});
+    else if (ch == 256) partial(dq, std::integral_constant<int, 256>{});
+    else partial(dq, std::integral_constant<int, 128>{});
+  };
+  if (d == 64) by_chunk(std::integral_constant<int, 64>{});
+  else by_chunk(std::integral_constant<int, 128>{});
   return hipGetLastError();
 }
 

@@ -65,10 +65,11 @@ hipError_t launch_fwd_fp8(const void* q, const void* k, const void* v, void* o, 
                           float scale, float dq, float dk, float dv, bool causal, hipStream_t stream);
 
 // Decode against a KV cache: Nq <= decode_max_queries() queries per
-// (batch, head), Nk cached keys, split into decode_chunks(Nk) chunks whose
-// partial results (m, l: BH*S*Nq floats each, then O: BH*S*Nq*d floats) live
-// in the fp32 workspace `ws`.
-int decode_chunks(int Nk);
+// (batch, head), Nk cached keys, split into S = decode_chunks(BH, Nk) chunks
+// (of 512, 256 or 128 keys, by the size of the call) whose partial results
+// (m, l: BH*S*Nq floats each, then O: BH*S*Nq*d floats) live in the fp32
+// workspace `ws`.
+int decode_chunks(int BH, int Nk);
 int decode_max_queries();
 hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, float* lse, float* ws, int BH,
                          int Nq, int Nk, int d, float scale, bool causal, hipStream_t stream);
