@@ -225,9 +225,21 @@ def test_dropout_validation(lib):
 
 def test_decode_workspace_and_validation(lib):
     INV, UNS = binding.ATTN_ERR_INVALID, binding.ATTN_ERR_UNSUPPORTED
-    # chunks of 512 keys; per chunk and query: m, l and d floats, rounded up to 256 bytes
-    assert lib.attn_decode_workspace_bytes(2, 3, 1, 1000, 128) == ((2 * 3 * 2 * 1 * 130 * 4 + 255) // 256) * 256
-    assert lib.attn_decode_workspace_bytes(1, 1, 8, 512, 64) == 8 * 66 * 4 + (256 - (8 * 66 * 4) % 256) % 256
+    # chunks of 512 keys, or 256 / 128 when 512 would give the call fewer than 1024 workgroups (B*H*chunks);
+    # per chunk and query: m, l and d floats, rounded up to 256 bytes
+    def chunks(BH, Nk):
+        for ch in (512, 256):
+            if BH * -(-Nk // ch) >= 1024:
+                return -(-Nk // ch)
+        return -(-Nk // 128)
+
+    def expect(B, H, Nq, Nk, d):
+        return ((B * H * chunks(B * H, Nk) * Nq * (d + 2) * 4 + 255) // 256) * 256
+
+    assert lib.attn_decode_workspace_bytes(2, 3, 1, 1000, 128) == expect(2, 3, 1, 1000, 128) == 25088  # 8 chunks of 128
+    assert lib.attn_decode_workspace_bytes(1, 1, 8, 512, 64) == expect(1, 1, 8, 512, 64) == 4 * 8 * 66 * 4
+    assert lib.attn_decode_workspace_bytes(4, 32, 8, 16384, 128) == expect(4, 32, 8, 16384, 128)  # 512-key chunks
+    assert chunks(128, 16384) == 32 and chunks(8, 32768) == 128 and chunks(1, 1 << 23) == (1 << 23) // 512
     assert lib.attn_decode_workspace_bytes(1, 1, 9, 512, 64) == 0
     assert lib.attn_decode_workspace_bytes(1, 1, 1, 0, 64) == 0
     assert lib.attn_decode_workspace_bytes(1, 1, 1, 100, 96) == 0
