@@ -43,14 +43,30 @@ constexpr int kDecTargetWgs = 1024;  // workgroups a call should have to fill th
 constexpr int kDecTile = 64;    // keys per pass-1 tile (4 threads per key)
 constexpr int kDecMaxQ = 8;     // most queries per call
 
+// A chunk's unnormalised O column goes to the workspace for the merge kernel;
+// when the whole cache is one chunk (S == 1) there is nothing to merge, and
+// the kernel writes what the merge would form from that single chunk,
+// O = O_c / l_c and L = (m_c + log2 l_c) ln 2 (O = 0 and L = -inf for a query
+// with no allowed key), so the call needs one launch, not two.
+__device__ __forceinline__ void emit(bf16* __restrict__ O, float* __restrict__ L, float* __restrict__ ws_o, int bh,
+                                     int s, int S, int nq, int qi, int D, int dd, float o, float m, float l) {
+  if (S > 1) {
+    ws_o[(((size_t)bh * S + s) * nq + qi) * D + dd] = o;
+    return;
+  }
+  const bool empty = l == 0.f;
+  O[((size_t)bh * nq + qi) * D + dd] = (bf16)(empty ? 0.f : o / l);
+  if (dd == 0) L[(size_t)bh * nq + qi] = empty ? -INFINITY : (m + log2f(l)) * kLn2;
+}
+
 // NQ: query capacity of the instantiation (>= nq); registers and LDS scale
 // with it.  The launcher instantiates it for one query only (more go to
 // decode_mma_kernel), which keeps many workgroups per CU in flight
 template <int D, int NQ, int CH>
 __global__ void __launch_bounds__(256)
 decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                      float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, int Nk, int nq,
-                      int S, float c, int causal) {
+                      float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o,
+                      bf16* __restrict__ O, float* __restrict__ L, int Nk, int nq, int S, float c, int causal) {
   constexpr int DP = D / 4;          // dims per thread in pass 1
   constexpr int G8 = D / 8;          // 8-dim groups in pass 2
   constexpr int KL = 256 / G8;       // key lanes in pass 2
@@ -58,6 +74,7 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
   __shared__ __attribute__((aligned(16))) uint32_t qs2[NQ][D / 2];  // q as packed bf16 pairs
   __shared__ float sc[NQ][CH];
   __shared__ __attribute__((aligned(16))) float red[4][NQ][D];
+  __shared__ float cm[NQ], cl[NQ];  // the chunk's max and exp-sum per query
 
   const int bh = blockIdx.x / S;
   const int s = blockIdx.x % S;
@@ -126,8 +143,12 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
     if (lane == 0) {
-      ws_m[((size_t)bh * S + s) * nq + qi] = m;
-      ws_l[((size_t)bh * S + s) * nq + qi] = l;
+      cm[qi] = m;
+      cl[qi] = l;
+      if (S > 1) {
+        ws_m[((size_t)bh * S + s) * nq + qi] = m;
+        ws_l[((size_t)bh * S + s) * nq + qi] = l;
+      }
     }
   }
   __syncthreads();
@@ -185,7 +206,7 @@ decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, co
   for (int idx = tid; idx < nq * D; idx += 256) {
     const int qi = idx / D, dd = idx % D;
     const float o = red[0][qi][dd] + red[1][qi][dd] + red[2][qi][dd] + red[3][qi][dd];
-    ws_o[(((size_t)bh * S + s) * nq + qi) * D + dd] = o;
+    emit(O, L, ws_o, bh, s, S, nq, qi, D, dd, o, cm[qi], cl[qi]);
   }
 }
 
@@ -220,8 +241,8 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 template <int D, int CH>
 __global__ void __launch_bounds__(256, 6)
 decode_mma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                  float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, int Nk, int nq, int S,
-                  float c, int causal) {
+                  float* __restrict__ ws_m, float* __restrict__ ws_l, float* __restrict__ ws_o, bf16* __restrict__ O,
+                  float* __restrict__ L, int Nk, int nq, int S, float c, int causal) {
   constexpr int KS = D / 32;                 // 32-dim steps of the score product
   constexpr int KPW = CH / 4;         // keys per wave
   constexpr int DPL = D / 16;                // value dims per lane (= products per p V step)
@@ -229,6 +250,7 @@ decode_mma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const 
   constexpr int SBUF = kDecMaxQ * CH > 4 * kDecMaxQ * D ? kDecMaxQ * CH : 4 * kDecMaxQ * D;
   __shared__ __attribute__((aligned(16))) float sbuf[SBUF];
   __shared__ __attribute__((aligned(16))) bf16 p16[kDecMaxQ][CH];
+  __shared__ float cm[kDecMaxQ], cl[kDecMaxQ];  // the chunk's max and exp-sum per query
   float (*sc)[CH] = reinterpret_cast<float (*)[CH]>(sbuf);
 
   const int bh = blockIdx.x / S;
@@ -294,8 +316,12 @@ decode_mma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const 
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
     if (lane == 0) {
-      ws_m[((size_t)bh * S + s) * nq + qi] = m;
-      ws_l[((size_t)bh * S + s) * nq + qi] = l;
+      cm[qi] = m;
+      cl[qi] = l;
+      if (S > 1) {
+        ws_m[((size_t)bh * S + s) * nq + qi] = m;
+        ws_l[((size_t)bh * S + s) * nq + qi] = l;
+      }
     }
   }
   __syncthreads();
@@ -359,7 +385,7 @@ decode_mma_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const 
     for (int idx = tid; idx < nq * D; idx += 256) {
       const int qi = idx / D, dd = idx % D;
       const float o = red[0][qi][dd] + red[1][qi][dd] + red[2][qi][dd] + red[3][qi][dd];
-      ws_o[(((size_t)bh * S + s) * nq + qi) * D + dd] = o;
+      emit(O, L, ws_o, bh, s, S, nq, qi, D, dd, o, cm[qi], cl[qi]);
     }
   }
 }
@@ -448,12 +474,14 @@ hipError_t launch_decode(const void* q, const void* k, const void* v, void* o, f
     // the matrix-core kernel measured faster from two queries up
     if (Nq == 1)
       hipLaunchKernelGGL((decode_partial_kernel<D, 1, CH>), dim3(BH * S), dim3(256), 0, stream, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, ws_m, ws_l, ws_o, Nk, Nq, S, c, (int)causal);
+                         (const bf16*)k, (const bf16*)v, ws_m, ws_l, ws_o, (bf16*)o, lse, Nk, Nq, S, c, (int)causal);
     else
       hipLaunchKernelGGL((decode_mma_kernel<D, CH>), dim3(BH * S), dim3(256), 0, stream, (const bf16*)q,
-                         (const bf16*)k, (const bf16*)v, ws_m, ws_l, ws_o, Nk, Nq, S, c, (int)causal);
-    hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(BH * Nq), dim3(D), 0, stream, ws_m, ws_l, ws_o, (bf16*)o, lse,
-                       Nq, S);
+                         (const bf16*)k, (const bf16*)v, ws_m, ws_l, ws_o, (bf16*)o, lse, Nk, Nq, S, c, (int)causal);
+    // a single chunk wrote O and L itself
+    if (S > 1)
+      hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(BH * Nq), dim3(D), 0, stream, ws_m, ws_l, ws_o, (bf16*)o,
+                         lse, Nq, S);
   };
   auto by_chunk = [&](auto dq) {
     if (ch == 512) partial(dq, std::integral_constant<int, 512>{});
