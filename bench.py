@@ -22,7 +22,8 @@ still computed, so the FLOP counts are the dense ones).
 the bf16 forward on the same shape beside it, priced against the fp8 peak.
 --decode NQ times attn_decode: NQ new queries per head against a KV cache of
 --decode-nk keys (B=4, H=32, d=128 unless --batch/--heads say otherwise),
-priced against HBM bandwidth (it reads each cached key and value once).
+priced against HBM bandwidth (it reads each cached key and value once);
+--graph captures the K timed calls in one HIP graph and times its replay.
 
 --warmup W untimed steps come first.  For the first tens of milliseconds after
 the GPU leaves idle its clock is still ramping and the kernels run 10-20%
@@ -87,6 +88,8 @@ def parse():
                          "atomics, exp2 accuracy) and print their rates")
     ap.add_argument("--decode", type=int, default=None, help="time attn_decode with this many queries per head")
     ap.add_argument("--decode-nk", type=int, default=16384, help="cached keys per head for --decode")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --decode: capture the K timed calls in one HIP graph and time its replay")
     ap.add_argument("--flush-l2", action="store_true",
                     help="write a 512 MiB scratch buffer before every step, so no input is left in L2 or the MALL")
     ap.add_argument("--block-density", type=float, default=None,
@@ -485,12 +488,30 @@ def bench_decode(args):
 
     for _ in range(args.warmup):
         step()
+    graph = None
+    if args.graph:
+        # the K calls are captured back to back in one graph (attn_decode only enqueues kernels), so the
+        # timed replay shows the GPU's time per call without the host's launch cost of each call
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                step()
+        graph.replay()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record(stream)
-    for _ in range(args.steps):
-        step()
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(args.steps):
+            step()
     ev[1].record(stream)
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
@@ -515,7 +536,8 @@ def bench_decode(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "decode", "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "causal": True},
+        "config": {"workload": "decode", "B": B, "H": H, "Nq": Nq, "Nk": Nk, "d": d, "causal": True,
+                   "graph": bool(args.graph)},
         "gpu_ms_per_call": round(t_gpu, 4),
         "tflops": round(4.0 * d * Nq * Nk * B * H / (t_gpu * 1e-3) / 1e12, 3),
         "roofline": {"kernel": "decode (partial + merge)", "bound": "hbm", "achieved": round(gbs, 1),

@@ -74,3 +74,34 @@ def test_decode_is_deterministic(attn):
     b = attn.decode(q.cuda(), k.cuda(), v.cuda(), causal=True)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d", [(1, 8, 4, 3000, 128), (2, 3, 2, 100, 64), (1, 4, 1, 5000, 128)])
+def test_decode_replays_in_a_graph(attn, B, H, Nq, Nk, d):
+    """attn_decode enqueues kernels only (no allocation, no memset, no host sync), so it can be captured in a
+    HIP graph; every replay, with new queries copied in between, matches an eager call bit for bit.  The
+    shapes take the merged path (several chunks) and the single-chunk path."""
+    _say(f"decode graph B={B} H={H} Nq={Nq} Nk={Nk} d={d}")
+    q, k, v = draw(B, H, Nq, Nk, d, 5970 + Nk)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=qd.device)
+    ws = torch.empty(max(attn.decode_workspace_bytes(B, H, Nq, Nk, d), 1), dtype=torch.uint8, device=qd.device)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        attn.decode(qd, kd, vd, causal=True, out=o, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        attn.decode(qd, kd, vd, causal=True, out=o, lse=lse, workspace=ws)
+    for r in range(4):
+        qn = draw(B, H, Nq, 1, d, 6100 + 17 * r)[0]
+        qd.copy_(qn.cuda())
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        eo, el = attn.decode(qd, kd, vd, causal=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o, eo) and torch.equal(lse, el), f"replay {r}"
