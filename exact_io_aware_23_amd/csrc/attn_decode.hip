@@ -12,7 +12,7 @@
 // cores.  The work is split over the keys:
 //   * decode_partial_kernel (one query) or decode_mma_kernel (two or more,
 //     both products on the matrix cores; see there): one workgroup per
-//     (batch*head, 512-key chunk).  In the first, four threads per key form
+//     (batch*head, chunk of 512 keys, or 256 / 128 for small calls).  In the first, four threads per key form
 //     the chunk's scores for every query (16-byte loads of K kept as bf16
 //     pairs, v_dot2_f32_bf16 against q held in LDS as bf16 pairs, two DPP
 //     adds); one wave per query takes the chunk max and exp-sum; then 16
@@ -37,11 +37,11 @@
 namespace attn {
 namespace {
 
-constexpr int kDecChunk = 512;  // keys per workgroup, most (a call with few heads and keys takes 256 or 128)
-constexpr int kDecMinChunk = 128;
+constexpr int kDecChunk = 512;       // keys per workgroup at most (small calls take 256 or 128)
+constexpr int kDecMinChunk = 128;    // keys per workgroup at least
 constexpr int kDecTargetWgs = 1024;  // workgroups a call should have to fill the GPU (four per CU)
-constexpr int kDecTile = 64;    // keys per pass-1 tile (4 threads per key)
-constexpr int kDecMaxQ = 8;     // most queries per call
+constexpr int kDecTile = 64;         // keys per pass-1 tile (4 threads per key)
+constexpr int kDecMaxQ = 8;          // most queries per call
 
 // A chunk's unnormalised O column goes to the workspace for the merge kernel;
 // when the whole cache is one chunk (S == 1) there is nothing to merge, and
@@ -61,7 +61,8 @@ __device__ __forceinline__ void emit(bf16* __restrict__ O, float* __restrict__ L
 
 // NQ: query capacity of the instantiation (>= nq); registers and LDS scale
 // with it.  The launcher instantiates it for one query only (more go to
-// decode_mma_kernel), which keeps many workgroups per CU in flight
+// decode_mma_kernel), which keeps many workgroups per CU in flight.  CH: keys
+// per chunk (512, 256 or 128).
 template <int D, int NQ, int CH>
 __global__ void __launch_bounds__(256)
 decode_partial_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
